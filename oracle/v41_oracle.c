@@ -1,0 +1,422 @@
+/*
+ * Plain CPU oracle for the hot path of DeepSeek-V4.1 compressed sparse
+ * attention: the fp8 round trip of kv rows, the window selection, the indexer
+ * score, the index top-k and the sparse attention with a per-head sink.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  The GPU library
+ * shares no code, header, table or helper with it, and it includes nothing
+ * from that library.  It is deliberately slow: scalar loops, one element at a
+ * time, in double precision, with a single rounding to the output type.
+ *
+ * Sources (the pages this follows):
+ *  - "deepseek_v41_ref::attn" rustdoc, module description and the function
+ *    contracts act_quant_inplace, pow2_ceil, window_topk_idxs, sparse_attn
+ *    (precision contract; ring-cache example).
+ *  - "Compressed sparse attention" layer page (atlas, reindex layer,
+ *    p=1000), section "All 25 steps": the FP8(W) step, the indexer score
+ *    S^I, the top-512 selection I_t, the window set J^w_t, the join Y/J/G_t
+ *    and the sink softmax A and O.
+ *  - "attn_v41.rs" source page, module documentation (selection width
+ *    limit, -1 = absent, indices offset past the window rows) and the
+ *    AttnV41Run struct (q after RoPE, rows_a / rows_b, idx layout).
+ *
+ * Readings taken where the pages are silent (each is listed with its reason
+ * in the design notes of the repository):
+ *  - e4m3 is the OCP E4M3FN format (bias 7, 3 fraction bits, subnormals,
+ *    largest finite 448, no infinities): the page's 448 rules out E4M3FNUZ.
+ *  - The fp8 block is 32 consecutive values along a row.
+ *  - A negative value that rounds to zero keeps its sign (-0).
+ *  - The top-k breaks ties by the lower position; +0 and -0 are equal;
+ *    -inf and NaN scores are excluded; fewer than k valid positions are
+ *    padded with -1.  The output is in (score desc, position asc) order.
+ *  - The softmax subtracts m = max(sink_h, max_i s_i) before exp: the
+ *    result is the same real number, it only avoids overflow of exp.
+ *  - Index values outside [0, rows_a_len + rows_b_len) are skipped like -1.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------ */
+/* bf16 <-> double                                                     */
+/* ------------------------------------------------------------------ */
+
+/* bf16 is the top 16 bits of an IEEE binary32; widening is exact. */
+double ora_bf16_to_double(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/*
+ * Round a double to the nearest bf16, ties to even, in one step.
+ * bf16: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits.
+ * Normal numbers in [2^-126, 2^128) have a quantum of 2^(E-7) where
+ * E = floor(log2|x|); below 2^-126 the quantum is the subnormal step
+ * 2^-133.  A magnitude that rounds to 2^128 or more overflows to inf.
+ */
+uint16_t ora_double_to_bf16(double x)
+{
+    if (isnan(x))
+        return 0x7FC0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0x0000;
+    double a = fabs(x);
+    if (a == 0.0)
+        return sign;
+    if (isinf(a))
+        return sign | 0x7F80;
+    int e2;
+    frexp(a, &e2);             /* a = m * 2^e2, m in [0.5, 1) */
+    int E = e2 - 1;            /* floor(log2 a) */
+    int qexp = (E < -126) ? -133 : E - 7;
+    double q = ldexp(1.0, qexp);
+    double r = nearbyint(a / q) * q;  /* default mode: to nearest, ties even */
+    if (r >= ldexp(1.0, 128))
+        return sign | 0x7F80;
+    float rf = (float)r;              /* exact: r is on the bf16 grid */
+    uint32_t u;
+    memcpy(&u, &rf, sizeof u);
+    return sign | (uint16_t)(u >> 16);
+}
+
+/* ------------------------------------------------------------------ */
+/* fp8 round trip (act_quant_inplace; FP8(W) step)                     */
+/* ------------------------------------------------------------------ */
+
+/*
+ * pow2_ceil: 2^ceil(log2 v) for a positive normal binary32 v, from the IEEE
+ * fields: a value whose fraction field is zero is already a power of two;
+ * otherwise the result is the power of two one above its exponent.
+ */
+float ora_pow2_ceil(float v)
+{
+    uint32_t u;
+    memcpy(&u, &v, sizeof u);
+    uint32_t exp_field = (u >> 23) & 0xFFu;
+    uint32_t frac_field = u & 0x7FFFFFu;
+    uint32_t out_exp = exp_field + (frac_field != 0 ? 1u : 0u);
+    uint32_t r = out_exp << 23;
+    float f;
+    memcpy(&f, &r, sizeof f);
+    return f;
+}
+
+/*
+ * Round y (|y| <= 448 after the clamp) to the nearest OCP E4M3FN value, ties
+ * to even.  E4M3FN normal numbers are 1.fff * 2^(e-7), e = 1..15, so in the
+ * binade [2^E, 2^(E+1)) the quantum is 2^(E-3); below 2^-6 the subnormals
+ * 0.fff * 2^-6 have the quantum 2^-9.  The sign of y is kept, zero included.
+ */
+double ora_e4m3_round(double y)
+{
+    double a = fabs(y);
+    double r;
+    if (a == 0.0) {
+        r = 0.0;
+    } else {
+        int e2;
+        frexp(a, &e2);
+        int E = e2 - 1;
+        int qexp = (E < -6) ? -9 : E - 3;
+        double q = ldexp(1.0, qexp);
+        r = nearbyint(a / q) * q;
+    }
+    return copysign(r, y);
+}
+
+/*
+ * One block of n values (n = 32 in the method): amax over the block, floored
+ * at 1e-4 (binary32), scale = pow2_ceil(amax / 448) with the division done in
+ * binary32, each value divided by the scale, clamped to +-448, rounded to
+ * e4m3, multiplied back by the scale and rounded to bf16.
+ */
+static void fp8_round_block(const uint16_t *in, uint16_t *out, int n)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < n; ++i) {
+        float v = (float)fabs(ora_bf16_to_double(in[i]));  /* exact */
+        if (v > amax)
+            amax = v;
+    }
+    if (amax < 1e-4f)
+        amax = 1e-4f;
+    float s = ora_pow2_ceil(amax / 448.0f);
+    for (int i = 0; i < n; ++i) {
+        double x = ora_bf16_to_double(in[i]);
+        double y = x / (double)s;           /* exact: s is a power of two */
+        if (y > 448.0)
+            y = 448.0;
+        if (y < -448.0)
+            y = -448.0;
+        double e = ora_e4m3_round(y);
+        out[i] = ora_double_to_bf16(e * (double)s);
+    }
+}
+
+/*
+ * Rows of row_len bf16 values (row_len a multiple of block); in and out may
+ * be the same buffer.  Returns 0, or -1 for a row_len that is not a multiple
+ * of the block.
+ */
+int ora_fp8_round_rows(const uint16_t *in, uint16_t *out, int64_t rows,
+                       int32_t row_len, int32_t block)
+{
+    if (block <= 0 || row_len % block != 0)
+        return -1;
+    uint16_t tmp[4096];
+    if (block > 4096)
+        return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int32_t c = 0; c < row_len; c += block) {
+            const uint16_t *src = in + r * (int64_t)row_len + c;
+            fp8_round_block(src, tmp, block);
+            memcpy(out + r * (int64_t)row_len + c, tmp,
+                   sizeof(uint16_t) * (size_t)block);
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* window selection (window_topk_idxs; J^w_t)                          */
+/* ------------------------------------------------------------------ */
+
+/*
+ * start_pos == 0: one causal window per query into the chunk itself,
+ *   cols = min(n_tokens, window); query t sees chunk rows
+ *   max(0, t - window + 1) .. t in ascending order, then -1.
+ * start_pos > 0: one query (the token at start_pos); the whole ring, oldest
+ *   first: slot (start_pos + 1 + c) mod window once the ring has wrapped
+ *   (start_pos >= window - 1); before that slots 0..start_pos, then -1.
+ * Writes idx[n_tokens][cols] and returns cols, or -1 when start_pos > 0 and
+ * n_tokens != 1.
+ */
+int ora_window_idx(int64_t start_pos, int32_t n_tokens, int32_t window,
+                   int32_t *idx)
+{
+    if (start_pos == 0) {
+        int32_t cols = n_tokens < window ? n_tokens : window;
+        for (int32_t t = 0; t < n_tokens; ++t) {
+            int32_t lo = t - window + 1;
+            if (lo < 0)
+                lo = 0;
+            for (int32_t c = 0; c < cols; ++c) {
+                int32_t slot = lo + c;
+                idx[(int64_t)t * cols + c] = (slot <= t) ? slot : -1;
+            }
+        }
+        return cols;
+    }
+    if (n_tokens != 1)
+        return -1;
+    for (int32_t c = 0; c < window; ++c) {
+        if (start_pos >= window - 1)
+            idx[c] = (int32_t)((start_pos + 1 + c) % window);
+        else
+            idx[c] = (c <= start_pos) ? c : -1;
+    }
+    return window;
+}
+
+/* ------------------------------------------------------------------ */
+/* indexer score (S^I) for one query                                   */
+/* ------------------------------------------------------------------ */
+
+/* Causal count of compressed positions visible to the token at position pos:
+ * floor((pos + 1) / ratio), capped at the rows present. */
+int64_t ora_causal_count(int64_t pos, int32_t ratio, int64_t n_rows)
+{
+    int64_t n = (pos + 1) / ratio;
+    return n < n_rows ? n : n_rows;
+}
+
+/*
+ * S[j] = sum_h w[h] * ReLU( sum_d qI[h][d] * kI[j][d] ) for j < n_valid and,
+ * when cand is given, cand[j / cand_block] != 0; every other j gets -inf.
+ * qI: [n_heads][head_dim] bf16, kI: [n_rows][head_dim] bf16 (one key per
+ * compressed position, shared by all heads), w: [n_heads] f32.
+ */
+void ora_indexer_scores_one(const uint16_t *qI, const uint16_t *kI,
+                            const float *w, const uint8_t *cand,
+                            int32_t cand_block, int32_t n_heads,
+                            int32_t head_dim, int64_t n_rows, int64_t n_valid,
+                            double *out)
+{
+    for (int64_t j = 0; j < n_rows; ++j) {
+        int allowed = j < n_valid;
+        if (allowed && cand != NULL && cand[j / cand_block] == 0)
+            allowed = 0;
+        if (!allowed) {
+            out[j] = -INFINITY;
+            continue;
+        }
+        double total = 0.0;
+        for (int32_t h = 0; h < n_heads; ++h) {
+            double dot = 0.0;
+            for (int32_t d = 0; d < head_dim; ++d)
+                dot += ora_bf16_to_double(qI[(int64_t)h * head_dim + d]) *
+                       ora_bf16_to_double(kI[j * head_dim + d]);
+            double relu = dot > 0.0 ? dot : 0.0;
+            total += (double)w[h] * relu;
+        }
+        out[j] = total;
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* index top-k (I_t = top_k(S^I ...))                                  */
+/* ------------------------------------------------------------------ */
+
+struct ora_scored {
+    double s;
+    int64_t j;
+};
+
+/* Order: higher score first; equal scores (+0 == -0) by lower position. */
+static int cmp_scored(const void *pa, const void *pb)
+{
+    const struct ora_scored *a = (const struct ora_scored *)pa;
+    const struct ora_scored *b = (const struct ora_scored *)pb;
+    if (a->s > b->s)
+        return -1;
+    if (a->s < b->s)
+        return 1;
+    if (a->j < b->j)
+        return -1;
+    if (a->j > b->j)
+        return 1;
+    return 0;
+}
+
+/*
+ * Valid positions are those whose score is neither -inf nor NaN.  Writes the
+ * m = min(k, #valid) best positions plus offset, in (score desc, position
+ * asc) order, then -1 up to k entries.  Returns m, or -1 on allocation
+ * failure.
+ */
+int64_t ora_topk_one(const double *scores, int64_t n, int32_t k,
+                     int32_t offset, int32_t *out)
+{
+    struct ora_scored *v = (struct ora_scored *)malloc(
+        sizeof(struct ora_scored) * (size_t)(n > 0 ? n : 1));
+    if (v == NULL)
+        return -1;
+    int64_t nv = 0;
+    for (int64_t j = 0; j < n; ++j) {
+        double s = scores[j];
+        if (isnan(s) || (isinf(s) && s < 0))
+            continue;
+        v[nv].s = s;
+        v[nv].j = j;
+        ++nv;
+    }
+    qsort(v, (size_t)nv, sizeof(struct ora_scored), cmp_scored);
+    int64_t m = nv < k ? nv : k;
+    for (int32_t i = 0; i < k; ++i)
+        out[i] = (i < m) ? (int32_t)(v[i].j + offset) : -1;
+    free(v);
+    return m;
+}
+
+/* ------------------------------------------------------------------ */
+/* sparse attention with the sink (S, A, O steps; sparse_attn)         */
+/* ------------------------------------------------------------------ */
+
+/*
+ * The gathered row for joint index ix: rows_a (the window rows) for
+ * ix < rows_a_len, rows_b (the compressed rows) for the rest; NULL when ix
+ * is -1 or out of range.
+ */
+static const uint16_t *gather_row(int64_t ix, const uint16_t *rows_a,
+                                  int64_t rows_a_len, const uint16_t *rows_b,
+                                  int64_t rows_b_len, int32_t head_dim)
+{
+    if (ix < 0)
+        return NULL;
+    if (ix < rows_a_len)
+        return rows_a + ix * head_dim;
+    if (rows_b != NULL && ix - rows_a_len < rows_b_len)
+        return rows_b + (ix - rows_a_len) * head_dim;
+    return NULL;
+}
+
+/*
+ * Attention weights of one head of one query: for each idx entry i, A_i =
+ * exp(s_i) / (exp(sink) + sum_j exp(s_j)) with s_i = scale * q . g_i, and 0
+ * for skipped entries.  Also returns the sink's share exp(sink) / den.
+ * Scores are shifted by m = max(sink, max_i s_i) before exp.
+ */
+double ora_attn_weights_one_head(const uint16_t *q_h, const uint16_t *rows_a,
+                                 int64_t rows_a_len, const uint16_t *rows_b,
+                                 int64_t rows_b_len, const int32_t *idx,
+                                 int32_t width, float sink, double scale,
+                                 int32_t head_dim, double *weights)
+{
+    double m = (double)sink;
+    for (int32_t i = 0; i < width; ++i) {
+        const uint16_t *g = gather_row(idx[i], rows_a, rows_a_len, rows_b,
+                                       rows_b_len, head_dim);
+        if (g == NULL) {
+            weights[i] = -INFINITY;
+            continue;
+        }
+        double dot = 0.0;
+        for (int32_t d = 0; d < head_dim; ++d)
+            dot += ora_bf16_to_double(q_h[d]) * ora_bf16_to_double(g[d]);
+        weights[i] = dot * scale;
+        if (weights[i] > m)
+            m = weights[i];
+    }
+    double den = exp((double)sink - m);
+    for (int32_t i = 0; i < width; ++i)
+        if (!isinf(weights[i]))
+            den += exp(weights[i] - m);
+    for (int32_t i = 0; i < width; ++i)
+        weights[i] = isinf(weights[i]) ? 0.0 : exp(weights[i] - m) / den;
+    return exp((double)sink - m) / den;
+}
+
+/*
+ * One query, all heads: o[h] = sum_i A_{h,i} g_i, rounded to bf16.
+ * q: [n_heads][head_dim], sink: [n_heads], out: [n_heads][head_dim].
+ * A query with no valid index gets o = 0.  Returns 0, or -1 on allocation
+ * failure.
+ */
+int ora_sparse_attn_one(const uint16_t *q, const uint16_t *rows_a,
+                        int64_t rows_a_len, const uint16_t *rows_b,
+                        int64_t rows_b_len, const int32_t *idx, int32_t width,
+                        const float *sink, double scale, int32_t n_heads,
+                        int32_t head_dim, uint16_t *out)
+{
+    double *wts = (double *)malloc(sizeof(double) * (size_t)(width > 0 ? width : 1));
+    double *acc = (double *)malloc(sizeof(double) * (size_t)head_dim);
+    if (wts == NULL || acc == NULL) {
+        free(wts);
+        free(acc);
+        return -1;
+    }
+    for (int32_t h = 0; h < n_heads; ++h) {
+        const uint16_t *q_h = q + (int64_t)h * head_dim;
+        ora_attn_weights_one_head(q_h, rows_a, rows_a_len, rows_b, rows_b_len,
+                                  idx, width, sink[h], scale, head_dim, wts);
+        for (int32_t d = 0; d < head_dim; ++d)
+            acc[d] = 0.0;
+        for (int32_t i = 0; i < width; ++i) {
+            const uint16_t *g = gather_row(idx[i], rows_a, rows_a_len, rows_b,
+                                           rows_b_len, head_dim);
+            if (g == NULL)
+                continue;
+            for (int32_t d = 0; d < head_dim; ++d)
+                acc[d] += wts[i] * ora_bf16_to_double(g[d]);
+        }
+        for (int32_t d = 0; d < head_dim; ++d)
+            out[(int64_t)h * head_dim + d] = ora_double_to_bf16(acc[d]);
+    }
+    free(wts);
+    free(acc);
+    return 0;
+}
