@@ -1,0 +1,203 @@
+/*
+ * v41.h -- C ABI of the MI355X (gfx950) hot path of DeepSeek-V4.1 compressed
+ * sparse attention: fp8 round trip of kv rows, window selection, indexer
+ * score, index top-k, and sparse attention with a per-head sink.
+ *
+ * Conventions shared by every call
+ *  - bf16 values travel as raw uint16 bit patterns (v41_bf16).
+ *  - Every data pointer is a device pointer owned by the caller; the library
+ *    keeps no state between calls.  Only the calls with a `workspace`
+ *    argument use scratch memory, and only the caller's.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
+ *    stream) and never synchronise the host.
+ *  - Strides ("_ld" between rows, "_bs" between sequences) count elements,
+ *    not bytes.
+ *  - Return value: 0 on success; V41_EINVAL (-1) for an invalid argument,
+ *    V41_EHIP (-2) for a HIP runtime or launch error, V41_EDEVICE (-3) when
+ *    the current device is not a gfx950.  v41_last_error() then returns a
+ *    message (thread-local, valid until the next call on the thread).
+ *  - Index values that the host cannot see (idx contents) are not checked:
+ *    an entry outside [0, rows_a_len + rows_b_len) is skipped like -1.
+ *
+ * Sources: the "deepseek_v41_ref::attn" rustdoc (function contracts
+ * act_quant_inplace, pow2_ceil, window_topk_idxs, sparse_attn, the precision
+ * paragraph and the ring-cache example); the "Compressed sparse attention"
+ * layer page, section "All 25 steps" (FP8(W), S^I, I_t, J^w_t, the join
+ * Y/J/G_t, the sink softmax A and O); the "attn_v41.rs" source page (module
+ * invariants, SharedV41 and AttnV41Run).
+ */
+#ifndef V41_H
+#define V41_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t v41_bf16;
+typedef void *v41_stream;
+
+#define V41_OK 0
+#define V41_EINVAL (-1)
+#define V41_EHIP (-2)
+#define V41_EDEVICE (-3)
+
+/* Values per fp8 scale block (the rustdoc's FP8_BLOCK). */
+#define V41_FP8_BLOCK 32
+/* Widest selection sparse attention accepts (window + top-k), as in the
+ * attn_v41.rs module invariant on the sparse_attn score buffer. */
+#define V41_MAX_WIDTH 2048
+/* Largest indexer head count one call takes. */
+#define V41_MAX_INDEX_HEADS 64
+
+/* Message for the last non-zero status on this thread ("" if none). */
+const char *v41_last_error(void);
+
+/* ABI revision of this header. */
+int v41_abi_version(void);
+
+/*
+ * fp8 round trip of kv rows ("deepseek_v41_ref::attn": act_quant_inplace and
+ * pow2_ceil; "Compressed sparse attention", All 25 steps: W <- FP8(W)).
+ *
+ * For every row and every block of 32 consecutive values: amax = max |x|,
+ * floored at 1e-4; s = 2^ceil(log2(amax / 448)) (binary32 division, exponent
+ * from the IEEE fields); each x goes to x / s, clamped to +-448, rounded to
+ * the nearest OCP E4M3FN value (ties to even, subnormals kept, sign of zero
+ * kept), multiplied by s and stored as bf16.  The stored value is exact
+ * (e4m3 times a power of two) except when it reaches 2^128, which rounds to
+ * +-inf in bf16.
+ *
+ *   in       [rows][in_ld] bf16; the first row_len values of each row are read
+ *   out      [rows][out_ld] bf16; may equal `in` (same ld) for in place.
+ *            Pointing `out` at a ring slot with out_ld = one sequence's ring
+ *            stride writes a batch of decode rows into their slots.
+ *   row_len  multiple of 32, > 0; in_ld, out_ld >= row_len, multiples of 8
+ *   ring     optional (NULL = none) window ring [ring_slots][row_len]: row r
+ *            is token first_pos + r, and each of the last
+ *            min(rows, ring_slots) rows is also written to ring slot
+ *            (first_pos + r) mod ring_slots (the prefill's ring seeding).
+ *   in, out, ring: 16-byte aligned.
+ */
+int v41_fp8_round_rows(const v41_bf16 *in, int64_t in_ld, v41_bf16 *out,
+                       int64_t out_ld, int64_t rows, int32_t row_len,
+                       v41_bf16 *ring, int32_t ring_slots, int64_t first_pos,
+                       v41_stream stream);
+
+/*
+ * Window selection ("deepseek_v41_ref::attn": window_topk_idxs; "Compressed
+ * sparse attention", All 25 steps: J^w_t = {max(0, t-127) .. t}).
+ *
+ *   start_pos == 0: cols = min(n_tokens, window); token t gets chunk rows
+ *     max(0, t - window + 1) .. t ascending, then -1 up to cols.
+ *   start_pos > 0: n_tokens must be 1; cols = window; the whole ring oldest
+ *     first: slot (start_pos + 1 + c) mod window once start_pos >= window - 1,
+ *     else slots 0 .. start_pos then -1.
+ *   idx       int32 [batch][n_tokens][idx_ld] at idx + b*idx_bs + t*idx_ld
+ *             (the first cols entries are written; the same for every b)
+ *   cols_out  host pointer (nullable): receives cols.
+ */
+int v41_window_idx(int64_t start_pos, int32_t n_tokens, int32_t window,
+                   int32_t batch, int32_t *idx, int64_t idx_ld, int64_t idx_bs,
+                   int32_t *cols_out, v41_stream stream);
+
+/*
+ * Indexer score ("Compressed sparse attention", All 25 steps:
+ * S^I_{t,j} = sum_h w^I_{t,h} ReLU(Q^I_{h,t} . K^I_j), visible for
+ * j < floor((t+1)/ratio) and where the candidate mask M^c allows).
+ *
+ * Query q = b * n_tokens + t is the token at position start_pos + t of
+ * sequence b; it sees n(q) = min(n_rows, floor((start_pos + t + 1) / ratio))
+ * compressed positions, further limited by cand[q][j / cand_block] != 0 when
+ * cand is given.  Every other column of its score row is -inf.
+ *
+ *   qI      bf16 [batch * n_tokens][n_heads][head_dim]
+ *   kI      bf16 [batch] x [n_rows][head_dim] at kI + b*kI_bs (one key per
+ *           compressed position, shared by all heads)
+ *   w       f32 [batch * n_tokens][n_heads] (the 1/sqrt scaling already in)
+ *   cand    u8 [batch * n_tokens][cand_width] or NULL; cand_block > 0
+ *   scores  f32 [batch * n_tokens][scores_ld], scores_ld >= n_rows
+ *   n_heads 1 .. 64; head_dim 32, 64 or 128; ratio >= 1; n_rows >= 0.
+ * Products are bf16 x bf16 exact, accumulated in f32 on the matrix cores;
+ * ReLU, the weights and the head sum in f32.
+ */
+int v41_indexer_scores(const v41_bf16 *qI, const v41_bf16 *kI, int64_t kI_bs,
+                       const float *w, const uint8_t *cand, int32_t cand_width,
+                       int32_t cand_block, int32_t batch, int32_t n_tokens,
+                       int64_t start_pos, int32_t ratio, int32_t n_heads,
+                       int32_t head_dim, int64_t n_rows, float *scores,
+                       int64_t scores_ld, v41_stream stream);
+
+/*
+ * Index top-k ("Compressed sparse attention", All 25 steps: I_t = top_k of
+ * S^I over the visible positions; "attn_v41.rs": the selection is offset past
+ * the window rows and -1 marks an absent entry).
+ *
+ * Per score row: valid positions are those whose score is neither -inf nor
+ * NaN.  The m = min(k, #valid) best are written as position + offset, in
+ * order of score descending then position ascending (equal scores, with +0
+ * equal to -0, go to the lower position), followed by -1 up to k entries.
+ *
+ *   scores  f32 [n_sel_rows][scores_ld], n_cols <= scores_ld
+ *   idx     int32 [n_sel_rows][idx_ld]; entries 0 .. k-1 of each row are
+ *           written (point it at the first compressed column of the joint
+ *           index buffer)
+ *   k       1 .. 2048
+ */
+int v41_topk_select(const float *scores, int64_t n_sel_rows, int64_t n_cols,
+                    int64_t scores_ld, int32_t k, int32_t offset, int32_t *idx,
+                    int64_t idx_ld, v41_stream stream);
+
+/*
+ * Sparse attention with the sink ("Compressed sparse attention", All 25
+ * steps: G_t = Y[J_t], S = Q . G / sqrt(d), A = exp S / (exp s_h +
+ * sum exp S), O = sum A G; "deepseek_v41_ref::attn": sparse_attn, f32 softmax,
+ * -1 skipped, bf16 out; "attn_v41.rs": AttnV41Run).
+ *
+ * For query q = b * n_tokens + t and head h: the valid entries i of
+ * idx[q][0 .. width) select row g_i = rows_a[b][ix] when ix < rows_a_len and
+ * rows_b[b][ix - rows_a_len] otherwise; s_i = scale * (q_h . g_i);
+ * o_h = sum_i exp(s_i) g_i / (exp(sink_h) + sum_i exp(s_i)).  One latent row
+ * is both key and value.  A query with no valid entry gets o = 0.
+ *
+ *   q       bf16 [batch * n_tokens][n_heads][head_dim] (after RoPE)
+ *   rows_a  bf16 [batch] x [rows_a_len][head_dim] at rows_a + b*a_bs (window
+ *           rows: the chunk's own fp8-rounded rows at a prefill, the ring at
+ *           a decode)
+ *   rows_b  bf16 [batch] x [rows_b_len][head_dim] at rows_b + b*b_bs (the
+ *           compressed latent rows); may be NULL only if rows_b_len == 0
+ *   idx     int32 [batch * n_tokens][idx_ld], width <= min(idx_ld, 2048)
+ *   sink    f32 [n_heads]; scale: f32 (1/sqrt(head_dim) in the method)
+ *   out     bf16 [batch * n_tokens][n_heads][head_dim]
+ *   head_dim 64, 128, 256 or 512; n_heads >= 1.
+ *   workspace / workspace_bytes: optional device scratch (NULL / 0 allowed).
+ *           With at least v41_sparse_attn_workspace_bytes(...) bytes the
+ *           call may split one query's rows over several workgroups; with
+ *           less it does not split.  The result is the same either way up to
+ *           f32 rounding order.  Calls that share a workspace must not
+ *           overlap in time.
+ * QK^T and PV run as bf16 products with f32 accumulation; the softmax is in
+ * f32; the probabilities enter PV rounded to bf16.
+ */
+int v41_sparse_attn_sink(const v41_bf16 *q, const v41_bf16 *rows_a,
+                         int64_t rows_a_len, int64_t a_bs,
+                         const v41_bf16 *rows_b, int64_t rows_b_len,
+                         int64_t b_bs, const int32_t *idx, int32_t width,
+                         int64_t idx_ld, const float *sink, float scale,
+                         int32_t batch, int32_t n_tokens, int32_t n_heads,
+                         int32_t head_dim, v41_bf16 *out, void *workspace,
+                         int64_t workspace_bytes, v41_stream stream);
+
+/* Workspace size that lets v41_sparse_attn_sink split rows as it prefers
+ * for this shape (0 when it would not split). */
+int64_t v41_sparse_attn_workspace_bytes(int32_t batch, int32_t n_tokens,
+                                        int32_t n_heads, int32_t head_dim,
+                                        int32_t width);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* V41_H */

@@ -1,0 +1,239 @@
+// C ABI of libv41: argument validation on the host, the gfx950 device check,
+// the thread-local last-error message, then one launcher per call.  The
+// contracts (and the passages of the pages they come from) are in
+// include/v41.h.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/v41.h"
+#include "v41_common.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+// 0 = unknown, 1 = gfx950, 2 = other device
+std::atomic<int> g_dev_kind[64];
+
+int check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(V41_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(V41_EDEVICE, "device ordinal %d out of range", dev);
+  int kind = g_dev_kind[dev].load(std::memory_order_relaxed);
+  if (kind == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(V41_EHIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    kind = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_dev_kind[dev].store(kind, std::memory_order_relaxed);
+    if (kind == 2)
+      return fail(V41_EDEVICE, "device %d is %s, this library is built for gfx950", dev,
+                  prop.gcnArchName);
+  }
+  if (kind == 2) return fail(V41_EDEVICE, "device %d is not a gfx950", dev);
+  return V41_OK;
+}
+
+int launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(V41_EHIP, "%s launch: %s", what, hipGetErrorString(e));
+  g_err[0] = '\0';
+  return V41_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* v41_last_error(void) { return g_err; }
+
+int v41_abi_version(void) { return 1; }
+
+int v41_fp8_round_rows(const v41_bf16* in, int64_t in_ld, v41_bf16* out, int64_t out_ld,
+                       int64_t rows, int32_t row_len, v41_bf16* ring, int32_t ring_slots,
+                       int64_t first_pos, v41_stream stream) {
+  if (rows < 0) return fail(V41_EINVAL, "fp8_round_rows: rows < 0");
+  if (row_len <= 0 || row_len % V41_FP8_BLOCK != 0)
+    return fail(V41_EINVAL, "fp8_round_rows: row_len %d is not a positive multiple of %d",
+                row_len, V41_FP8_BLOCK);
+  if (in_ld < row_len || out_ld < row_len || in_ld % 8 != 0 || out_ld % 8 != 0)
+    return fail(V41_EINVAL, "fp8_round_rows: in_ld/out_ld must be >= row_len and multiples of 8");
+  if (rows > 0 && (in == nullptr || out == nullptr))
+    return fail(V41_EINVAL, "fp8_round_rows: NULL in/out");
+  if (!aligned16(in) || !aligned16(out) || !aligned16(ring))
+    return fail(V41_EINVAL, "fp8_round_rows: pointers must be 16-byte aligned");
+  if (ring != nullptr && ring_slots <= 0)
+    return fail(V41_EINVAL, "fp8_round_rows: ring given with ring_slots <= 0");
+  if (ring != nullptr && first_pos < 0)
+    return fail(V41_EINVAL, "fp8_round_rows: first_pos < 0");
+  int rc = check_device();
+  if (rc) return rc;
+  return launched(v41::launch_fp8_round_rows(in, in_ld, out, out_ld, rows, row_len, ring,
+                                             ring_slots, first_pos, (hipStream_t)stream),
+                  "fp8_round_rows");
+}
+
+int v41_window_idx(int64_t start_pos, int32_t n_tokens, int32_t window, int32_t batch,
+                   int32_t* idx, int64_t idx_ld, int64_t idx_bs, int32_t* cols_out,
+                   v41_stream stream) {
+  if (start_pos < 0 || n_tokens < 0 || window <= 0 || batch < 0)
+    return fail(V41_EINVAL, "window_idx: negative start_pos/n_tokens/batch or window <= 0");
+  if (start_pos > 0 && n_tokens != 1)
+    return fail(V41_EINVAL, "window_idx: a decode call (start_pos > 0) takes one token, got %d",
+                n_tokens);
+  const int32_t cols = (start_pos == 0) ? (n_tokens < window ? n_tokens : window) : window;
+  if (idx_ld < cols) return fail(V41_EINVAL, "window_idx: idx_ld %lld < cols %d",
+                                 (long long)idx_ld, cols);
+  if (batch > 1 && idx_bs < (int64_t)n_tokens * idx_ld)
+    return fail(V41_EINVAL, "window_idx: idx_bs too small");
+  if (idx == nullptr && (int64_t)batch * n_tokens * cols > 0)
+    return fail(V41_EINVAL, "window_idx: NULL idx");
+  if (cols_out) *cols_out = cols;
+  int rc = check_device();
+  if (rc) return rc;
+  return launched(v41::launch_window_idx(start_pos, n_tokens, window, cols, batch, idx, idx_ld,
+                                         idx_bs, (hipStream_t)stream),
+                  "window_idx");
+}
+
+int v41_indexer_scores(const v41_bf16* qI, const v41_bf16* kI, int64_t kI_bs, const float* w,
+                       const uint8_t* cand, int32_t cand_width, int32_t cand_block,
+                       int32_t batch, int32_t n_tokens, int64_t start_pos, int32_t ratio,
+                       int32_t n_heads, int32_t head_dim, int64_t n_rows, float* scores,
+                       int64_t scores_ld, v41_stream stream) {
+  if (batch < 0 || n_tokens < 0 || n_rows < 0 || start_pos < 0)
+    return fail(V41_EINVAL, "indexer_scores: negative batch/n_tokens/n_rows/start_pos");
+  if (ratio < 1) return fail(V41_EINVAL, "indexer_scores: ratio %d < 1", ratio);
+  if (n_heads < 1 || n_heads > V41_MAX_INDEX_HEADS)
+    return fail(V41_EINVAL, "indexer_scores: n_heads %d outside 1..%d", n_heads,
+                V41_MAX_INDEX_HEADS);
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128)
+    return fail(V41_EINVAL, "indexer_scores: head_dim %d not in {32, 64, 128}", head_dim);
+  if (start_pos > 0 && n_tokens != 1)
+    return fail(V41_EINVAL, "indexer_scores: a decode call (start_pos > 0) takes one token");
+  if (scores_ld < n_rows) return fail(V41_EINVAL, "indexer_scores: scores_ld < n_rows");
+  if (batch > 1 && kI_bs < n_rows * head_dim)
+    return fail(V41_EINVAL, "indexer_scores: kI_bs < n_rows * head_dim");
+  if (kI_bs % 8 != 0) return fail(V41_EINVAL, "indexer_scores: kI_bs must be a multiple of 8");
+  const bool work = (int64_t)batch * n_tokens > 0 && n_rows > 0;
+  if (work && (qI == nullptr || kI == nullptr || w == nullptr || scores == nullptr))
+    return fail(V41_EINVAL, "indexer_scores: NULL qI/kI/w/scores (kI NULL means no latent "
+                            "index-key cache has been published)");
+  if (cand != nullptr && (cand_block < 1 || (int64_t)cand_width * cand_block < n_rows))
+    return fail(V41_EINVAL, "indexer_scores: candidate mask needs cand_block >= 1 and "
+                            "cand_width * cand_block >= n_rows");
+  if (!aligned16(qI) || !aligned16(kI))
+    return fail(V41_EINVAL, "indexer_scores: qI and kI must be 16-byte aligned");
+  int rc = check_device();
+  if (rc) return rc;
+  return launched(v41::launch_indexer_scores(qI, kI, kI_bs, w, cand, cand_width, cand_block,
+                                             batch, n_tokens, start_pos, ratio, n_heads,
+                                             head_dim, n_rows, scores, scores_ld,
+                                             (hipStream_t)stream),
+                  "indexer_scores");
+}
+
+int v41_topk_select(const float* scores, int64_t n_sel_rows, int64_t n_cols, int64_t scores_ld,
+                    int32_t k, int32_t offset, int32_t* idx, int64_t idx_ld,
+                    v41_stream stream) {
+  if (n_sel_rows < 0 || n_cols < 0) return fail(V41_EINVAL, "topk_select: negative size");
+  if (k < 1 || k > V41_MAX_WIDTH)
+    return fail(V41_EINVAL, "topk_select: k %d outside 1..%d", k, V41_MAX_WIDTH);
+  if (scores_ld < n_cols) return fail(V41_EINVAL, "topk_select: scores_ld < n_cols");
+  if (idx_ld < k) return fail(V41_EINVAL, "topk_select: idx_ld < k");
+  if (n_cols >= 0x7FFFFFFFLL) return fail(V41_EINVAL, "topk_select: n_cols too large");
+  if (n_sel_rows > 0 && (idx == nullptr || (scores == nullptr && n_cols > 0)))
+    return fail(V41_EINVAL, "topk_select: NULL scores/idx");
+  if (offset < 0 || (int64_t)offset + n_cols > 0x7FFFFFFFLL)
+    return fail(V41_EINVAL, "topk_select: offset out of range");
+  int rc = check_device();
+  if (rc) return rc;
+  return launched(v41::launch_topk_select(scores, n_sel_rows, n_cols, scores_ld, k, offset, idx,
+                                          idx_ld, (hipStream_t)stream),
+                  "topk_select");
+}
+
+int64_t v41_sparse_attn_workspace_bytes(int32_t batch, int32_t n_tokens, int32_t n_heads,
+                                        int32_t head_dim, int32_t width) {
+  if (batch <= 0 || n_tokens <= 0 || n_heads <= 0 || width <= 0) return 0;
+  const int32_t nq = batch * n_tokens;
+  return v41::attn_workspace_bytes(nq, n_heads, head_dim,
+                                   v41::attn_preferred_splits(nq, n_heads, width));
+}
+
+int v41_sparse_attn_sink(const v41_bf16* q, const v41_bf16* rows_a, int64_t rows_a_len,
+                         int64_t a_bs, const v41_bf16* rows_b, int64_t rows_b_len, int64_t b_bs,
+                         const int32_t* idx, int32_t width, int64_t idx_ld, const float* sink,
+                         float scale, int32_t batch, int32_t n_tokens, int32_t n_heads,
+                         int32_t head_dim, v41_bf16* out, void* workspace,
+                         int64_t workspace_bytes, v41_stream stream) {
+  if (batch < 0 || n_tokens < 0 || rows_a_len < 0 || rows_b_len < 0)
+    return fail(V41_EINVAL, "sparse_attn_sink: negative size");
+  if (n_heads < 1) return fail(V41_EINVAL, "sparse_attn_sink: n_heads < 1");
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256 && head_dim != 512)
+    return fail(V41_EINVAL, "sparse_attn_sink: head_dim %d not in {64, 128, 256, 512}",
+                head_dim);
+  if (width < 0 || width > V41_MAX_WIDTH)
+    return fail(V41_EINVAL, "sparse_attn_sink: width %d outside 0..%d (the selection limit)",
+                width, V41_MAX_WIDTH);
+  if (idx_ld < width) return fail(V41_EINVAL, "sparse_attn_sink: idx_ld < width");
+  if (rows_b == nullptr && rows_b_len > 0)
+    return fail(V41_EINVAL, "sparse_attn_sink: rows_b is NULL but rows_b_len = %lld (no "
+                            "latent cache published)",
+                (long long)rows_b_len);
+  if (rows_a_len + rows_b_len > 0x7FFFFFFFLL)
+    return fail(V41_EINVAL, "sparse_attn_sink: too many rows for int32 indices");
+  if (batch > 1 && (a_bs < rows_a_len * head_dim || (rows_b_len > 0 && b_bs < rows_b_len * head_dim)))
+    return fail(V41_EINVAL, "sparse_attn_sink: a_bs/b_bs smaller than one sequence's rows");
+  if (a_bs % 8 != 0 || b_bs % 8 != 0)
+    return fail(V41_EINVAL, "sparse_attn_sink: a_bs/b_bs must be multiples of 8");
+  const int64_t nq = (int64_t)batch * n_tokens;
+  if (nq > 0x7FFFFFFFLL) return fail(V41_EINVAL, "sparse_attn_sink: too many queries");
+  if (nq > 0 && (q == nullptr || out == nullptr || sink == nullptr ||
+                 (width > 0 && idx == nullptr) || (rows_a == nullptr && rows_a_len > 0)))
+    return fail(V41_EINVAL, "sparse_attn_sink: NULL q/out/sink/idx/rows_a");
+  if (!aligned16(q) || !aligned16(rows_a) || !aligned16(rows_b) || !aligned16(out) ||
+      !aligned16(workspace))
+    return fail(V41_EINVAL, "sparse_attn_sink: q/rows/out/workspace must be 16-byte aligned");
+  if (workspace_bytes < 0) return fail(V41_EINVAL, "sparse_attn_sink: workspace_bytes < 0");
+  int rc = check_device();
+  if (rc) return rc;
+  v41::AttnArgs a;
+  a.q = q;
+  a.rows_a = rows_a;
+  a.rows_a_len = rows_a_len;
+  a.a_bs = a_bs;
+  a.rows_b = rows_b;
+  a.rows_b_len = rows_b_len;
+  a.b_bs = b_bs;
+  a.idx = idx;
+  a.width = width;
+  a.idx_ld = idx_ld;
+  a.sink = sink;
+  a.scale = scale;
+  a.batch = batch;
+  a.n_tokens = n_tokens;
+  a.n_heads = n_heads;
+  a.head_dim = head_dim;
+  a.out = out;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace ? workspace_bytes : 0;
+  return launched(v41::launch_sparse_attn_sink(a, (hipStream_t)stream), "sparse_attn_sink");
+}
+
+}  // extern "C"

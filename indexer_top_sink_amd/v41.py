@@ -1,0 +1,136 @@
+"""Thin Python binding of libv41 (the gfx950 HIP library): one function per C
+entry point, with the same name and argument order.  It only marshals
+arguments -- tensors become device pointers, the stream defaults to torch's
+current stream -- and raises V41Error on a non-zero status.  There is no
+fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libv41.so")
+
+V41_OK, V41_EINVAL, V41_EHIP, V41_EDEVICE = 0, -1, -2, -3
+EXPORTS = ("v41_last_error", "v41_abi_version", "v41_fp8_round_rows", "v41_window_idx",
+           "v41_indexer_scores", "v41_topk_select", "v41_sparse_attn_sink",
+           "v41_sparse_attn_workspace_bytes")
+
+
+class V41Error(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libv41 status {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load() -> C.CDLL:
+    """Load libv41.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m indexer_top_sink_amd.build` (hipcc, gfx950)")
+    L = C.CDLL(LIB_PATH)
+    vp, i64, i32, f32 = C.c_void_p, C.c_int64, C.c_int32, C.c_float
+    L.v41_last_error.restype = C.c_char_p
+    L.v41_last_error.argtypes = []
+    L.v41_abi_version.restype = C.c_int
+    L.v41_abi_version.argtypes = []
+    L.v41_fp8_round_rows.restype = C.c_int
+    L.v41_fp8_round_rows.argtypes = [vp, i64, vp, i64, i64, i32, vp, i32, i64, vp]
+    L.v41_window_idx.restype = C.c_int
+    L.v41_window_idx.argtypes = [i64, i32, i32, i32, vp, i64, i64, C.POINTER(C.c_int32), vp]
+    L.v41_indexer_scores.restype = C.c_int
+    L.v41_indexer_scores.argtypes = [vp, vp, i64, vp, vp, i32, i32, i32, i32, i64, i32, i32,
+                                     i32, i64, vp, i64, vp]
+    L.v41_topk_select.restype = C.c_int
+    L.v41_topk_select.argtypes = [vp, i64, i64, i64, i32, i32, vp, i64, vp]
+    L.v41_sparse_attn_sink.restype = C.c_int
+    L.v41_sparse_attn_sink.argtypes = [vp, vp, i64, i64, vp, i64, i64, vp, i32, i64, vp, f32,
+                                       i32, i32, i32, i32, vp, vp, i64, vp]
+    L.v41_sparse_attn_workspace_bytes.restype = C.c_int64
+    L.v41_sparse_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    _lib = L
+    return L
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(rc: int) -> None:
+    if rc != V41_OK:
+        msg = load().v41_last_error()
+        raise V41Error(rc, msg.decode() if msg else "")
+
+
+def v41_last_error() -> str:
+    m = load().v41_last_error()
+    return m.decode() if m else ""
+
+
+def v41_abi_version() -> int:
+    return load().v41_abi_version()
+
+
+def v41_fp8_round_rows(inp, in_ld, out, out_ld, rows, row_len, ring=None, ring_slots=0,
+                       first_pos=0, stream=None) -> None:
+    _check(load().v41_fp8_round_rows(_ptr(inp), in_ld, _ptr(out), out_ld, rows, row_len,
+                                     _ptr(ring), ring_slots, first_pos, _stream(stream)))
+
+
+def v41_window_idx(start_pos, n_tokens, window, batch, idx, idx_ld, idx_bs,
+                   stream=None) -> int:
+    cols = C.c_int32(0)
+    _check(load().v41_window_idx(start_pos, n_tokens, window, batch, _ptr(idx), idx_ld, idx_bs,
+                                 C.byref(cols), _stream(stream)))
+    return cols.value
+
+
+def v41_indexer_scores(qI, kI, kI_bs, w, cand, cand_width, cand_block, batch, n_tokens,
+                       start_pos, ratio, n_heads, head_dim, n_rows, scores, scores_ld,
+                       stream=None) -> None:
+    _check(load().v41_indexer_scores(_ptr(qI), _ptr(kI), kI_bs, _ptr(w), _ptr(cand),
+                                     cand_width, cand_block, batch, n_tokens, start_pos, ratio,
+                                     n_heads, head_dim, n_rows, _ptr(scores), scores_ld,
+                                     _stream(stream)))
+
+
+def v41_topk_select(scores, n_sel_rows, n_cols, scores_ld, k, offset, idx, idx_ld,
+                    stream=None) -> None:
+    _check(load().v41_topk_select(_ptr(scores), n_sel_rows, n_cols, scores_ld, k, offset,
+                                  _ptr(idx), idx_ld, _stream(stream)))
+
+
+def v41_sparse_attn_sink(q, rows_a, rows_a_len, a_bs, rows_b, rows_b_len, b_bs, idx, width,
+                         idx_ld, sink, scale, batch, n_tokens, n_heads, head_dim, out,
+                         workspace=None, workspace_bytes=0, stream=None) -> None:
+    _check(load().v41_sparse_attn_sink(_ptr(q), _ptr(rows_a), rows_a_len, a_bs, _ptr(rows_b),
+                                       rows_b_len, b_bs, _ptr(idx), width, idx_ld, _ptr(sink),
+                                       float(scale), batch, n_tokens, n_heads, head_dim,
+                                       _ptr(out), _ptr(workspace), workspace_bytes,
+                                       _stream(stream)))
+
+
+def v41_sparse_attn_workspace_bytes(batch, n_tokens, n_heads, head_dim, width) -> int:
+    return int(load().v41_sparse_attn_workspace_bytes(batch, n_tokens, n_heads, head_dim,
+                                                      width))

@@ -1,0 +1,66 @@
+"""Comparison helpers for the GPU parity tests (tolerances of the method):
+fp8 rows, window indices and top-k indices bit-exact; indexer scores within
+1e-4 relative (infinities exact); attention outputs within 2 bf16 ulp or 1e-2
+absolute, with max ulp and max relative error reported."""
+from __future__ import annotations
+
+import numpy as np
+
+from inputs import synth as S
+
+SCORE_RTOL = 1e-4
+ATTN_ULPS = 2.0
+ATTN_ATOL = 1e-2
+
+
+def bf16_f64(h: np.ndarray) -> np.ndarray:
+    return S.bf16_bits_to_f32(h).astype(np.float64)
+
+
+def ulp_bf16(x: np.ndarray) -> np.ndarray:
+    """bf16 ulp at |x|: 2^(floor(log2|x|) - 7), floored at the ulp of the
+    smallest normal (2^-133)."""
+    a = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 7)
+
+
+def attn_report(gpu_bits: np.ndarray, ora_bits: np.ndarray) -> dict:
+    g, o = bf16_f64(gpu_bits), bf16_f64(ora_bits)
+    err = np.abs(g - o)
+    ulps = err / ulp_bf16(o)
+    ok = (ulps <= ATTN_ULPS) | (err <= ATTN_ATOL)
+    rel = err / np.maximum(np.abs(o), 1e-30)
+    return {
+        "n": int(o.size),
+        "fail": int((~ok).sum()),
+        "max_ulp": float(ulps.max()) if ulps.size else 0.0,
+        "frac_within_2ulp": float((ulps <= ATTN_ULPS).mean()) if ulps.size else 1.0,
+        "max_abs": float(err.max()) if err.size else 0.0,
+        "max_rel_nonzero": float(rel[np.abs(o) > 1e-6].max()) if (np.abs(o) > 1e-6).any() else 0.0,
+        "finite": bool(np.isfinite(g).all()),
+    }
+
+
+def assert_attn_close(gpu_bits, ora_bits, what=""):
+    r = attn_report(gpu_bits, ora_bits)
+    print(f"[attn parity] {what} {r}", flush=True)
+    assert r["finite"], what
+    assert r["fail"] == 0, (what, r)
+    return r
+
+
+def assert_scores_close(gpu: np.ndarray, ora: np.ndarray, what=""):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ora = np.asarray(ora, dtype=np.float64)
+    inf_o = np.isinf(ora)
+    assert np.array_equal(np.isinf(gpu), inf_o), (what, "infinity pattern differs")
+    assert np.array_equal(gpu[inf_o], ora[inf_o]), what
+    f = ~inf_o
+    err = np.abs(gpu[f] - ora[f])
+    tol = SCORE_RTOL * np.abs(ora[f]) + 1e-30
+    bad = err > tol
+    rel = float((err / np.maximum(np.abs(ora[f]), 1e-30)).max()) if f.any() else 0.0
+    print(f"[score parity] {what} n={int(f.sum())} max_rel={rel:.3e} fail={int(bad.sum())}",
+          flush=True)
+    assert not bad.any(), (what, int(bad.sum()), rel)
+    return rel

@@ -1,0 +1,103 @@
+"""The C ABI without a GPU: libv41.so loads, exports every entry point that
+include/v41.h declares, and rejects invalid arguments on the host (these
+calls return before any device work, so they run on the CPU)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "v41.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(v41_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from indexer_top_sink_amd import v41
+    if not os.path.exists(v41.LIB_PATH):
+        pytest.fail("libv41.so is not built (python -m indexer_top_sink_amd.build)")
+    return v41.load()
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("v41_fp8_round_rows", "v41_window_idx", "v41_indexer_scores",
+              "v41_topk_select", "v41_sparse_attn_sink"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    from indexer_top_sink_amd import v41
+    assert set(v41.EXPORTS) == set(declared_functions())
+
+
+def test_abi_version(lib):
+    assert lib.v41_abi_version() == 1
+
+
+def _err(lib):
+    return lib.v41_last_error().decode()
+
+
+def test_fp8_rejects_bad_row_len(lib):
+    rc = lib.v41_fp8_round_rows(None, 48, None, 48, 1, 48, None, 0, 0, None)
+    assert rc == -1 and "row_len" in _err(lib)
+
+
+def test_fp8_rejects_unaligned(lib):
+    rc = lib.v41_fp8_round_rows(16 + 2, 64, 32, 64, 1, 64, None, 0, 0, None)
+    assert rc == -1 and "aligned" in _err(lib)
+
+
+def test_window_rejects_multi_token_decode(lib):
+    cols = C.c_int32(0)
+    rc = lib.v41_window_idx(5, 2, 8, 1, 1024, 8, 16, C.byref(cols), None)
+    assert rc == -1 and "one token" in _err(lib)
+
+
+def test_indexer_rejects_missing_cache(lib):
+    rc = lib.v41_indexer_scores(1024, None, 0, 1024, None, 0, 1, 1, 1, 100, 4, 64, 128, 10,
+                                1024, 10, None)
+    assert rc == -1 and "kI NULL" in _err(lib)
+
+
+def test_indexer_rejects_ratio_and_heads(lib):
+    assert lib.v41_indexer_scores(1024, 1024, 0, 1024, None, 0, 1, 1, 1, 100, 0, 64, 128, 10,
+                                  1024, 10, None) == -1
+    assert "ratio" in _err(lib)
+    assert lib.v41_indexer_scores(1024, 1024, 0, 1024, None, 0, 1, 1, 1, 100, 4, 65, 128, 10,
+                                  1024, 10, None) == -1
+    assert lib.v41_indexer_scores(1024, 1024, 0, 1024, None, 0, 1, 1, 1, 100, 4, 64, 96, 10,
+                                  1024, 10, None) == -1
+
+
+def test_topk_rejects_k(lib):
+    assert lib.v41_topk_select(1024, 1, 10, 10, 0, 0, 1024, 10, None) == -1
+    assert lib.v41_topk_select(1024, 1, 10, 10, 2049, 0, 1024, 4096, None) == -1
+
+
+def test_attn_rejects_wide_selection_and_missing_rows(lib):
+    rc = lib.v41_sparse_attn_sink(1024, 1024, 128, 0, 1024, 10, 0, 1024, 2049, 4096, 1024,
+                                  C.c_float(0.1), 1, 1, 64, 512, 1024, None, 0, None)
+    assert rc == -1 and "width" in _err(lib)
+    rc = lib.v41_sparse_attn_sink(1024, 1024, 128, 0, None, 10, 0, 1024, 640, 640, 1024,
+                                  C.c_float(0.1), 1, 1, 64, 512, 1024, None, 0, None)
+    assert rc == -1 and "rows_b" in _err(lib)
+    rc = lib.v41_sparse_attn_sink(1024, 1024, 128, 0, None, 0, 0, 1024, 640, 640, 1024,
+                                  C.c_float(0.1), 1, 1, 64, 320, 1024, None, 0, None)
+    assert rc == -1 and "head_dim" in _err(lib)
+
+
+def test_workspace_query(lib):
+    # few queries: the call would split rows and asks for scratch
+    assert lib.v41_sparse_attn_workspace_bytes(64, 1, 64, 512, 640) > 0
+    # many queries: no split
+    assert lib.v41_sparse_attn_workspace_bytes(1, 2048, 64, 512, 640) == 0

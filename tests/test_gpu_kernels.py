@@ -1,0 +1,320 @@
+"""GPU parity of each libv41 call against the oracle, at sizes the oracle
+finishes in seconds that span several tiles and a ragged tail, plus edge
+cases (empty, ragged, degenerate).  Calls go through the C ABI binding."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from inputs import synth as S
+from parity import assert_attn_close, assert_scores_close
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def v41():
+    from indexer_top_sink_amd import v41 as m
+    m.load()
+    return m
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def up16(a):
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16))
+    return t.to(DEV)
+
+
+def down16(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy().view(np.uint16)
+
+
+def bf16_of(x):
+    return S.f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+# ------------------------------------------------------------------ fp8
+def all_finite_bf16_blocks():
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    x = S.bf16_bits_to_f32(allb)
+    fin = allb[np.isfinite(x)]
+    n = (fin.size // 32) * 32
+    srt = fin[np.argsort(x[np.isfinite(x)], kind="stable")][:n]
+    rng = np.random.default_rng(11)
+    return np.concatenate([srt, rng.permutation(fin)[:n]]).reshape(-1, 512)
+
+
+def test_fp8_exhaustive_bf16(v41):
+    rows = all_finite_bf16_blocks()
+    say("fp8 exhaustive", rows.shape)
+    d_in = up16(rows)
+    d_out = torch.empty_like(d_in)
+    v41.v41_fp8_round_rows(d_in, 512, d_out, 512, rows.shape[0], 512)
+    assert np.array_equal(down16(d_out), O.fp8_round_rows(rows))
+
+
+@pytest.mark.parametrize("rows,row_len,in_ld,out_ld", [(1, 32, 32, 32), (7, 64, 72, 80),
+                                                       (2048, 512, 512, 512), (3, 96, 96, 104)])
+def test_fp8_strided(v41, rows, row_len, in_ld, out_ld):
+    say("fp8 strided", rows, row_len, in_ld, out_ld)
+    rng = np.random.default_rng(rows)
+    x = bf16_of(rng.standard_normal((rows, in_ld)) * np.exp(rng.uniform(-20, 20, (rows, 1))))
+    d_in = up16(x)
+    d_out = torch.full((rows, out_ld), 0x1234, dtype=torch.int16, device=DEV)
+    v41.v41_fp8_round_rows(d_in, in_ld, d_out, out_ld, rows, row_len)
+    got = down16(d_out)
+    assert np.array_equal(got[:, :row_len], O.fp8_round_rows(x[:, :row_len]))
+    assert np.all(got[:, row_len:] == 0x1234)
+
+
+def test_fp8_in_place_and_ring(v41):
+    T, D, W = 12, 64, 8
+    say("fp8 ring", T, D, W)
+    rng = np.random.default_rng(5)
+    x = bf16_of(rng.standard_normal((T, D)))
+    d = up16(x)
+    ring = torch.zeros(W, D, dtype=torch.int16, device=DEV)
+    v41.v41_fp8_round_rows(d, D, d, D, T, D, ring, W, 0)
+    want = O.fp8_round_rows(x)
+    assert np.array_equal(down16(d), want)
+    cache = O.WindowCache(W, D)
+    cache.prefill(want)
+    assert np.array_equal(down16(ring), cache.rows)
+    assert cache.token.tolist() == [8, 9, 10, 11, 4, 5, 6, 7]
+
+
+def test_fp8_zero_rows(v41):
+    d = torch.zeros(1, 32, dtype=torch.int16, device=DEV)
+    v41.v41_fp8_round_rows(d, 32, d, 32, 0, 32)
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ window
+@pytest.mark.parametrize("start,T,W,B", [(0, 1, 8, 1), (0, 12, 8, 1), (0, 300, 128, 2),
+                                         (0, 2048, 128, 1), (12, 1, 8, 3), (13, 1, 8, 1),
+                                         (3, 1, 8, 2), (127, 1, 128, 1), (32767, 1, 128, 64),
+                                         (131071, 1, 128, 16)])
+def test_window(v41, start, T, W, B):
+    say("window", start, T, W, B)
+    cols = min(T, W) if start == 0 else W
+    ld = cols + 5
+    idx = torch.full((B, T, ld), -7, dtype=torch.int32, device=DEV)
+    got_cols = v41.v41_window_idx(start, T, W, B, idx, ld, T * ld)
+    torch.cuda.synchronize()
+    assert got_cols == cols
+    g = idx.cpu().numpy()
+    want = O.window_idx(start, T, W)
+    for b in range(B):
+        assert np.array_equal(g[b, :, :cols], want)
+    assert np.all(g[:, :, cols:] == -7)
+
+
+# ------------------------------------------------------------------ indexer
+def run_indexer(v41, qI, kI, w, start, ratio, cand=None, cand_block=1, B=1, T=None):
+    """qI [B*T, HI, DI], kI [B, L, DI], w [B*T, HI]"""
+    Q, HI, DI = qI.shape
+    L = kI.shape[1]
+    T = Q // B if T is None else T
+    d_s = torch.full((Q, L + 3), 7.0, dtype=torch.float32, device=DEV)
+    dc = torch.from_numpy(cand).to(DEV) if cand is not None else None
+    v41.v41_indexer_scores(up16(qI), up16(kI), L * DI, torch.from_numpy(w).to(DEV), dc,
+                           cand.shape[1] if cand is not None else 0, cand_block, B, T, start,
+                           ratio, HI, DI, L, d_s, L + 3)
+    torch.cuda.synchronize()
+    got = d_s.cpu().numpy()
+    assert np.all(got[:, L:] == 7.0)
+    return got[:, :L]
+
+
+@pytest.mark.parametrize("HI,DI,L,start,ratio,T,B", [
+    (64, 128, 1000, 4095, 4, 1, 1),     # decode, ragged tail
+    (64, 128, 333, 10 ** 6, 1, 1, 3),   # batch of decodes
+    (2, 32, 4, 0, 4, 12, 1),            # the tiny layer's prefill
+    (17, 64, 97, 0, 4, 400, 1),         # odd head count, causal prefill
+    (1, 32, 50, 10 ** 6, 1, 1, 1),
+    (48, 128, 512, 0, 4, 64, 1),
+])
+def test_indexer_parity(v41, HI, DI, L, start, ratio, T, B):
+    say("indexer", HI, DI, L, start, ratio, T, B)
+    rng = np.random.default_rng(HI * 1000 + L)
+    qI = bf16_of(rng.standard_normal((B * T, HI, DI)))
+    kI = bf16_of(rng.standard_normal((B, L, DI)))
+    w = (rng.uniform(0, 1, (B * T, HI)) / 8).astype(np.float32)
+    got = run_indexer(v41, qI, kI, w, start, ratio, B=B, T=T)
+    for b in range(B):
+        ora = O.indexer_scores(qI[b * T:(b + 1) * T], kI[b], w[b * T:(b + 1) * T], start, ratio)
+        assert_scores_close(got[b * T:(b + 1) * T], ora, f"indexer b={b}")
+
+
+def test_indexer_candidate_mask(v41):
+    T, HI, DI, L, blk = 256, 64, 128, 64, 8
+    say("indexer mask", T, L, blk)
+    rng = np.random.default_rng(77)
+    qI = bf16_of(rng.standard_normal((T, HI, DI)))
+    kI = bf16_of(rng.standard_normal((1, L, DI)))
+    w = (rng.uniform(0, 1, (T, HI)) / 64).astype(np.float32)
+    cand = (rng.uniform(size=(T, L // blk)) < 0.5).astype(np.uint8)
+    got = run_indexer(v41, qI, kI, w, 0, 4, cand=cand, cand_block=blk)
+    ora = O.indexer_scores(qI, kI[0], w, 0, 4, cand=cand, cand_block=blk)
+    assert_scores_close(got, ora, "masked")
+
+
+def test_indexer_zero_keys_give_zero(v41):
+    HI, DI, L = 64, 128, 96
+    rng = np.random.default_rng(8)
+    qI = bf16_of(rng.standard_normal((1, HI, DI)))
+    kI = np.zeros((1, L, DI), dtype=np.uint16)
+    w = np.full((1, HI), 1 / 64, dtype=np.float32)
+    got = run_indexer(v41, qI, kI, w, 10 ** 6, 1)
+    assert np.all(got == 0.0)
+
+
+# ------------------------------------------------------------------ top-k
+def run_topk(v41, s, k, offset):
+    R, L = s.shape
+    d_s = torch.from_numpy(np.ascontiguousarray(s, dtype=np.float32)).to(DEV)
+    d_i = torch.full((R, k + 2), -9, dtype=torch.int32, device=DEV)
+    v41.v41_topk_select(d_s, R, L, L, k, offset, d_i, k + 2)
+    torch.cuda.synchronize()
+    got = d_i.cpu().numpy()
+    assert np.all(got[:, k:] == -9)
+    return got[:, :k]
+
+
+def tie_scores(rng, R, L):
+    s = (np.round(rng.standard_normal((R, L)) * 4) / 4).astype(np.float32)
+    s[rng.uniform(size=(R, L)) < 0.05] = -np.inf
+    s[rng.uniform(size=(R, L)) < 0.02] = np.nan
+    z = rng.uniform(size=(R, L)) < 0.05
+    s[z] = np.where(rng.uniform(size=z.sum()) < 0.5, 0.0, -0.0)
+    return s
+
+
+@pytest.mark.parametrize("R,L,k,offset", [(1, 1, 1, 0), (3, 7, 4, 128), (5, 512, 512, 2048),
+                                          (4, 1000, 512, 128), (2, 4096, 512, 128),
+                                          (2, 5000, 100, 0), (2, 32768, 512, 128),
+                                          (1, 40000, 2048, 7), (64, 8192, 512, 128),
+                                          (8, 300, 2048, 3)])
+def test_topk_parity_ties(v41, R, L, k, offset):
+    say("topk", R, L, k, offset)
+    rng = np.random.default_rng(R * 7 + L)
+    s = tie_scores(rng, R, L)
+    got = run_topk(v41, s, k, offset)
+    want = O.topk(s, k, offset)
+    assert np.array_equal(got, want)
+
+
+def test_topk_continuous_scores(v41):
+    rng = np.random.default_rng(3)
+    s = (rng.uniform(0, 4, (16, 32768))).astype(np.float32)
+    got = run_topk(v41, s, 512, 128)
+    assert np.array_equal(got, O.topk(s, 512, 128))
+
+
+def test_topk_all_excluded_and_signed_zeros(v41):
+    s = np.full((3, 600), -np.inf, dtype=np.float32)
+    s[1, :] = np.nan
+    s[2, ::2] = -0.0
+    s[2, 1::2] = 0.0
+    got = run_topk(v41, s, 512, 5)
+    want = O.topk(s, 512, 5)
+    assert np.array_equal(got, want)
+    assert np.all(got[0] == -1) and np.all(got[1] == -1)
+    assert got[2].tolist() == [5 + j for j in range(512)]
+
+
+def test_topk_big_tie_group_straddles_k(v41):
+    L, k = 32768, 512
+    rng = np.random.default_rng(9)
+    s = rng.uniform(0, 1, (2, L)).astype(np.float32)
+    pos = rng.permutation(L)[:301]
+    s[:, pos] = np.sort(s[0])[-400]
+    got = run_topk(v41, s, k, 128)
+    assert np.array_equal(got, O.topk(s, k, 128))
+
+
+# ------------------------------------------------------------------ attention
+def run_attn(v41, q, rows_a, rows_b, idx, sink, scale, B, T, use_ws=True):
+    """q [B*T, H, D]; rows_a [B, A, D]; rows_b [B, Lb, D] or None; idx [B*T, width]."""
+    Q, H, D = q.shape
+    A = rows_a.shape[1]
+    Lb = rows_b.shape[1] if rows_b is not None else 0
+    width = idx.shape[1]
+    d_out = torch.zeros(Q, H, D, dtype=torch.int16, device=DEV)
+    ws_bytes = v41.v41_sparse_attn_workspace_bytes(B, T, H, D, width) if use_ws else 0
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=DEV) if ws_bytes else None
+    v41.v41_sparse_attn_sink(up16(q), up16(rows_a), A, A * D,
+                             up16(rows_b) if rows_b is not None else None, Lb, Lb * D,
+                             torch.from_numpy(np.ascontiguousarray(idx, np.int32)).to(DEV),
+                             width, width, torch.from_numpy(sink).to(DEV), scale, B, T, H, D,
+                             d_out, ws, ws_bytes)
+    return down16(d_out)
+
+
+def oracle_attn(q, rows_a, rows_b, idx, sink, scale, B, T):
+    outs = []
+    for b in range(B):
+        outs.append(O.sparse_attn(q[b * T:(b + 1) * T], rows_a[b],
+                                  rows_b[b] if rows_b is not None else None,
+                                  idx[b * T:(b + 1) * T], sink, scale))
+    return np.concatenate(outs)
+
+
+@pytest.mark.parametrize("B,T,H,D,A,Lb,width,use_ws", [
+    (1, 1, 64, 512, 128, 1024, 640, True),     # decode, split rows
+    (1, 1, 64, 512, 128, 1024, 640, False),    # decode, no workspace
+    (3, 1, 64, 512, 128, 700, 640, True),
+    (1, 40, 64, 512, 40, 100, 168, True),      # prefill-like, many -1
+    (1, 12, 4, 64, 12, 4, 10, True),           # the tiny layer
+    (2, 3, 70, 128, 50, 60, 97, True),         # heads over two groups, ragged
+    (1, 5, 16, 256, 33, 0, 33, True),          # no compressed rows
+])
+def test_attn_parity(v41, B, T, H, D, A, Lb, width, use_ws):
+    say("attn", B, T, H, D, A, Lb, width, use_ws)
+    rng = np.random.default_rng(B * 100 + H + D)
+    q = bf16_of(rng.standard_normal((B * T, H, D)))
+    rows_a = bf16_of(rng.standard_normal((B, A, D)))
+    rows_b = bf16_of(rng.standard_normal((B, Lb, D))) if Lb > 0 else None
+    idx = rng.integers(-1, A + Lb, (B * T, width)).astype(np.int32)
+    idx[rng.uniform(size=idx.shape) < 0.2] = -1
+    idx[:, -1] = A + Lb + 5          # out of range: skipped
+    sink = rng.standard_normal(H).astype(np.float32)
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    got = run_attn(v41, q, rows_a, rows_b, idx, sink, scale, B, T, use_ws)
+    want = oracle_attn(q, rows_a, rows_b, idx, sink, scale, B, T)
+    assert_attn_close(got, want, f"B{B} T{T} H{H} D{D} w{width} ws{use_ws}")
+
+
+def test_attn_all_absent_and_one_row(v41):
+    H, D = 64, 512
+    rng = np.random.default_rng(1)
+    q = bf16_of(rng.standard_normal((2, H, D)))
+    rows_a = bf16_of(rng.standard_normal((1, 8, D)))
+    idx = np.full((2, 16), -1, dtype=np.int32)
+    idx[1, 5] = 3
+    sink = rng.standard_normal(H).astype(np.float32)
+    got = run_attn(v41, q, rows_a, None, idx, sink, 0.0625, 1, 2)
+    assert np.all(got[0] == 0)
+    want = oracle_attn(q, rows_a, None, idx, sink, 0.0625, 1, 2)
+    assert_attn_close(got, want, "one row")
+
+
+def test_attn_large_logits(v41):
+    """Scores far from zero exercise the running max (no overflow)."""
+    H, D, A = 64, 512, 300
+    rng = np.random.default_rng(4)
+    q = bf16_of(rng.standard_normal((1, H, D)) * 4)
+    rows_a = bf16_of(rng.standard_normal((1, A, D)) * 4)
+    idx = rng.permutation(A)[None, :].astype(np.int32)
+    sink = (rng.standard_normal(H) * 30).astype(np.float32)
+    got = run_attn(v41, q, rows_a, None, idx, sink, 0.044194173, 1, 1)
+    want = oracle_attn(q, rows_a, None, idx, sink, 0.044194173, 1, 1)
+    assert_attn_close(got, want, "large logits")
