@@ -1,0 +1,384 @@
+"""Benchmark of the compressed-sparse-attention hot path on one MI355X.
+
+A step is one pass of the whole path (fp8 round trip + ring write, window
+indices, indexer scores, top-k, sparse attention with the sink) over one batch
+of synthetic input already resident in HBM.  The default workload is the
+batched decode: 64 sequences at context 32768 (8192 compressed rows each),
+64 heads x 512, window 128, indexer 64 x 128, top-512; a step decodes one
+token per sequence.  The prefill chunk (2048 tokens at position 0) is
+reported alongside.
+
+Input staging rotates several copies of every input tensor, so a step never
+reads what the previous step left in the 256 MB last-level cache (as in a
+model, where the other layers run in between).  Each step is captured once in
+a HIP graph per copy and replayed; per-kernel durations come from HIP events
+around graph replays of single kernels on the same stream.  The CPU baseline
+is the oracle (plain C, one thread) on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode64]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from inputs import workloads as WL  # noqa: E402
+
+METRIC = "decode tokens/s + prefill tokens/s per layer; % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------- staging
+def geometry(wl):
+    from indexer_top_sink_amd.layer import Geometry
+    return Geometry(n_heads=wl.n_heads, head_dim=wl.head_dim, window=wl.window,
+                    index_heads=wl.index_heads, index_dim=wl.index_dim, topk=wl.topk,
+                    ratio=wl.ratio, scale=wl.scale)
+
+
+def stage_decode(wl, device, keep_host=False):
+    """Device buffers of a decode workload with its inputs uploaded; the ring
+    rows are rounded through fp8 on the GPU (they were written by earlier
+    steps).  Returns (buffers, host inputs or None)."""
+    import torch
+
+    from indexer_top_sink_amd import layer as LY
+    from indexer_top_sink_amd import v41
+    buf = LY.alloc_decode(geometry(wl), wl.batch, wl.n_rows, device)
+    host = [] if keep_host else None
+    for b in range(wl.batch):
+        d = WL.decode_sequence(wl, b)
+        buf.ring[b].copy_(LY.to_device_bf16(d["ring_raw"], device))
+        buf.kv_new[b].copy_(LY.to_device_bf16(d["kv_new"][0], device))
+        buf.latent[b].copy_(LY.to_device_bf16(d["latent"], device))
+        buf.kI[b].copy_(LY.to_device_bf16(d["kI"], device))
+        buf.qI[b].copy_(LY.to_device_bf16(d["qI"][0], device))
+        buf.w[b].copy_(torch.from_numpy(d["w"][0]).to(device))
+        buf.q[b].copy_(LY.to_device_bf16(d["q"][0], device))
+        if keep_host:
+            host.append(d)
+    buf.sink.copy_(torch.from_numpy(WL.layer_sink(wl)).to(device))
+    D = wl.head_dim
+    v41.v41_fp8_round_rows(buf.ring, D, buf.ring, D, wl.batch * wl.window, D)
+    torch.cuda.synchronize()
+    return buf, host
+
+
+def stage_prefill(wl, device, keep_host=False):
+    import torch
+
+    from indexer_top_sink_amd import layer as LY
+    d = WL.prefill_inputs(wl)
+    buf = LY.alloc_prefill(geometry(wl), wl.n_tokens, wl.n_rows, wl.cand_width,
+                           wl.cand_block, device)
+    buf.kv_chunk.copy_(LY.to_device_bf16(d["kv_chunk"], device))
+    buf.latent.copy_(LY.to_device_bf16(d["latent"], device))
+    buf.kI.copy_(LY.to_device_bf16(d["kI"], device))
+    buf.qI.copy_(LY.to_device_bf16(d["qI"], device))
+    buf.w.copy_(torch.from_numpy(d["w"]).to(device))
+    buf.q.copy_(LY.to_device_bf16(d["q"], device))
+    buf.cand.copy_(torch.from_numpy(d["cand"]).to(device))
+    buf.sink.copy_(torch.from_numpy(WL.layer_sink(wl)).to(device))
+    torch.cuda.synchronize()
+    return buf, (d if keep_host else None)
+
+
+def clone_buffers(buf):
+    """Another copy of every tensor of a buffer set (same values)."""
+    import copy
+
+    import torch
+    new = copy.copy(buf)
+    for k, v in vars(buf).items():
+        if isinstance(v, torch.Tensor):
+            setattr(new, k, v.clone())
+    return new
+
+
+# ----------------------------------------------------------------- the steps
+def step_calls(buf, mode):
+    """The five calls of one step as separate closures (kernel order)."""
+    from indexer_top_sink_amd import layer as LY
+    from indexer_top_sink_amd import v41
+    g = buf.geo
+    D, W = g.head_dim, g.window
+    if mode == "decode":
+        B, L, width, pos = buf.batch, buf.n_rows, buf.width, buf.pos
+        slot = pos % W
+        ws_bytes = buf.workspace.numel() if buf.workspace is not None else 0
+        return [
+            ("fp8_round_rows", lambda: v41.v41_fp8_round_rows(
+                buf.kv_new, D, buf.ring.data_ptr() + 2 * slot * D, W * D, B, D)),
+            ("window_idx", lambda: v41.v41_window_idx(pos, 1, W, B, buf.idx, width, width)),
+            ("indexer_scores", lambda: v41.v41_indexer_scores(
+                buf.qI, buf.kI, L * g.index_dim, buf.w, None, 0, 1, B, 1, pos, g.ratio,
+                g.index_heads, g.index_dim, L, buf.scores, L)),
+            ("topk_select", lambda: v41.v41_topk_select(
+                buf.scores, B, L, L, g.topk, W, buf.idx.data_ptr() + 4 * W, width)),
+            ("sparse_attn_sink", lambda: v41.v41_sparse_attn_sink(
+                buf.q, buf.ring, W, W * D, buf.latent, L, L * D, buf.idx, width, width,
+                buf.sink, g.scale, B, 1, g.n_heads, D, buf.out, buf.workspace, ws_bytes)),
+        ]
+    T, L, width, cols = buf.n_tokens, buf.n_rows, buf.width, buf.cols
+    cw = buf.cand.shape[1] if buf.cand is not None else 0
+    return [
+        ("fp8_round_rows", lambda: v41.v41_fp8_round_rows(
+            buf.kv_chunk, D, buf.rows_a, D, T, D, buf.ring, W, 0)),
+        ("window_idx", lambda: v41.v41_window_idx(0, T, W, 1, buf.idx, width, T * width)),
+        ("indexer_scores", lambda: v41.v41_indexer_scores(
+            buf.qI, buf.kI, L * g.index_dim, buf.w, buf.cand, cw, buf.cand_block, 1, T, 0,
+            g.ratio, g.index_heads, g.index_dim, L, buf.scores, L)),
+        ("topk_select", lambda: v41.v41_topk_select(
+            buf.scores, T, L, L, g.topk, T, buf.idx.data_ptr() + 4 * cols, width)),
+        ("sparse_attn_sink", lambda: v41.v41_sparse_attn_sink(
+            buf.q, buf.rows_a, T, T * D, buf.latent, L, L * D, buf.idx, width, width, buf.sink,
+            g.scale, 1, T, g.n_heads, D, buf.out, None, 0)),
+    ]
+
+
+def capture(fns, torch):
+    """One HIP graph replaying fns in order on a side stream."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for f in fns:      # warm the launch path before capture
+            f()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_replays(graphs, reps, torch):
+    """Mean ms per replay over `reps` replays cycling through `graphs`."""
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for i in range(reps):
+        graphs[i % len(graphs)].replay()
+    e1.record(st)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+# ----------------------------------------------------------------- algorithmic work
+def algorithmic(wl, host_idx=None, valid_pairs=None):
+    """Bytes and flops per kernel of one step (what the method must move or
+    compute).  Attention flops count 4 * H * D per valid index entry; indexer
+    flops 2 * HI * DI per visible (query, position) pair."""
+    H, D, HI, DI, W = wl.n_heads, wl.head_dim, wl.index_heads, wl.index_dim, wl.window
+    Q, L = wl.queries, wl.n_rows
+    if wl.mode == "decode":
+        pairs = Q * L if valid_pairs is None else valid_pairs
+        idx_valid = Q * wl.width if host_idx is None else int((host_idx >= 0).sum())
+        fp8_rows = Q
+    else:
+        pairs = valid_pairs
+        idx_valid = int((host_idx >= 0).sum())
+        fp8_rows = wl.n_tokens
+    k = {}
+    k["fp8_round_rows"] = {"bytes": fp8_rows * D * 2 * 2, "flops": 0}
+    k["window_idx"] = {"bytes": Q * wl.window_cols * 4, "flops": 0}
+    k["indexer_scores"] = {"bytes": pairs * DI * 2 + Q * HI * DI * 2 + Q * HI * 4 + Q * L * 4,
+                           "flops": pairs * 2 * HI * DI}
+    if wl.mode == "prefill":
+        # the index keys are read once per chunk; each visible pair reuses them
+        k["indexer_scores"]["bytes"] = L * DI * 2 + Q * HI * DI * 2 + Q * HI * 4 + Q * L * 4 + \
+            Q * wl.cand_width
+    k["topk_select"] = {"bytes": Q * L * 4 + Q * wl.topk * 4, "flops": 0}
+    rows_bytes = idx_valid * D * 2
+    if wl.mode == "prefill":
+        rows_bytes = (wl.n_tokens + L) * D * 2   # every row source read once
+    k["sparse_attn_sink"] = {"bytes": rows_bytes + Q * wl.width * 4 + 2 * Q * H * D * 2,
+                             "flops": idx_valid * 4 * H * D}
+    return k
+
+
+# ----------------------------------------------------------------- CPU baseline
+def cpu_baseline(wl, n_sample, budget_s=30.0):
+    """The oracle (plain C, one thread) on the first sequences / tokens of the
+    same workload; tokens per second scaled from the sample."""
+    import oracle as O
+    from oracle import layer as OL
+    sink = WL.layer_sink(wl)
+    t_total = 0.0
+    done = 0
+    if wl.mode == "decode":
+        for b in range(n_sample):
+            d = WL.decode_sequence(wl, b)
+            ring = O.WindowCache(wl.window, wl.head_dim)
+            ring.rows[:] = O.fp8_round_rows(d["ring_raw"])
+            t0 = time.perf_counter()
+            OL.decode(ring, d["kv_new"], wl.start_pos, d["q"], sink, wl.scale, ratio=wl.ratio,
+                      latent=d["latent"], kI=d["kI"], qI=d["qI"], w=d["w"], k=wl.topk)
+            t_total += time.perf_counter() - t0
+            done += 1
+            if t_total > budget_s:
+                break
+        sample = f"{done} of {wl.batch} sequences, one decode step each"
+    else:
+        d = WL.prefill_inputs(wl)
+        toks = list(range(wl.n_tokens - n_sample, wl.n_tokens))   # the costliest tokens
+        t0 = time.perf_counter()
+        OL.prefill(d["kv_chunk"], d["q"], sink, wl.scale, wl.window, ratio=wl.ratio,
+                   latent=d["latent"], kI=d["kI"], qI=d["qI"], w=d["w"], cand=d["cand"],
+                   cand_block=wl.cand_block, k=wl.topk, queries=toks)
+        t_total = time.perf_counter() - t0
+        done = len(toks)
+        sample = f"the last {done} of {wl.n_tokens} prefill tokens (the longest rows)"
+    return {"value": done / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": sample, "seconds": round(t_total, 3)}
+
+
+# ----------------------------------------------------------------- main
+def run_workload(name, steps, warmup, n_sets, torch, device):
+    from indexer_top_sink_amd import layer as LY
+    wl = WL.WORKLOADS[name]
+    t0 = time.time()
+    if wl.mode == "decode":
+        buf0, _ = stage_decode(wl, device)
+        buf0.pos = wl.start_pos
+    else:
+        buf0, _ = stage_prefill(wl, device)
+    sets = [buf0] + [clone_buffers(buf0) for _ in range(n_sets - 1)]
+    for s in sets:
+        s.pos = getattr(buf0, "pos", 0)
+    log(f"{name}: staged {n_sets} input sets in {time.time() - t0:.1f}s")
+
+    calls = [step_calls(s, wl.mode) for s in sets]
+    step_graphs = [capture([f for _, f in c], torch) for c in calls]
+    for i in range(warmup):
+        step_graphs[i % n_sets].replay()
+    torch.cuda.synchronize()
+    ms_step = time_replays(step_graphs, steps, torch)
+    log(f"{name}: {ms_step * 1e3:.1f} us per step")
+
+    # per-kernel durations: graphs of one kernel each, replayed over the sets
+    kern_us = {}
+    for ki, (kname, _) in enumerate(calls[0]):
+        gs = [capture([c[ki][1]], torch) for c in calls]
+        for i in range(3):
+            gs[i % n_sets].replay()
+        kern_us[kname] = time_replays(gs, max(steps, 20), torch) * 1e3
+    # restore a consistent state (the index buffer is rebuilt by a full step)
+    step_graphs[0].replay()
+    torch.cuda.synchronize()
+
+    idx = sets[0].idx.cpu().numpy()
+    pairs = None
+    if wl.mode == "prefill":
+        cand = sets[0].cand.cpu().numpy()
+        pairs = 0
+        for t in range(wl.n_tokens):
+            n = min(wl.n_rows, (t + 1) // wl.ratio)
+            blocks = np.repeat(cand[t].astype(bool), wl.cand_block)[:n]
+            pairs += int(blocks.sum())
+    work = algorithmic(wl, host_idx=idx, valid_pairs=pairs)
+    return wl, ms_step, kern_us, work
+
+
+def roofline_entry(kname, work, us, bound):
+    w = work[kname]
+    if bound == "hbm":
+        achieved = w["bytes"] / (us * 1e-6) / 1e9
+        peak, unit = HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved = w["flops"] / (us * 1e-6) / 1e12
+        peak, unit = BF16_PEAK_TFLOPS, "TFLOP/s"
+    return {"kernel": kname, "bound": bound, "achieved": round(achieved, 1), "peak": peak,
+            "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
+            "avg_us": round(us, 2), "algorithmic_bytes": w["bytes"],
+            "algorithmic_flops": w["flops"]}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode64", choices=sorted(WL.WORKLOADS))
+    ap.add_argument("--input-sets", type=int, default=3)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); each GPU would "
+              "take its own shard of sequences or tokens with no exchange, so run one "
+              "process per GPU", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    device = torch.device("cuda:0")
+    torch.cuda.set_device(device)
+    from indexer_top_sink_amd import v41
+    v41.load()
+
+    wl, ms_step, kern_us, work = run_workload(args.workload, args.steps, args.warmup,
+                                              args.input_sets, torch, device)
+    tokens = wl.queries
+    value = tokens / (ms_step * 1e-3)
+    dominant = max(work, key=lambda k: work[k]["bytes"])
+    if wl.mode == "prefill":
+        dominant = "sparse_attn_sink"
+    bound = "mfma" if wl.mode == "prefill" else "hbm"
+    roof = roofline_entry(dominant, work, kern_us[dominant], bound)
+
+    step_bytes = sum(v["bytes"] for v in work.values())
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "mode": wl.mode, "batch": wl.batch,
+                   "tokens_per_step": tokens, "position": wl.start_pos,
+                   "compressed_rows": wl.n_rows, "heads": wl.n_heads,
+                   "head_dim": wl.head_dim, "window": wl.window,
+                   "index_heads": wl.index_heads, "index_dim": wl.index_dim,
+                   "topk": wl.topk, "ratio": wl.ratio, "hip_graph": True,
+                   "input_sets": args.input_sets},
+        "roofline": roof,
+        "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "kernels_us": {k: round(v, 2) for k, v in kern_us.items()},
+    }
+    if not args.no_secondary and wl.name != "prefill":
+        pw, pms, pk, pwork = run_workload("prefill", max(10, args.steps // 2), 3,
+                                          args.input_sets, torch, device)
+        out["secondary"] = {
+            "prefill": {
+                "value": round(pw.n_tokens / (pms * 1e-3), 1), "unit": "tokens/s",
+                "ms_per_step": round(pms, 5),
+                "roofline": roofline_entry("sparse_attn_sink", pwork, pk["sparse_attn_sink"],
+                                           "mfma"),
+                "indexer_roofline": roofline_entry("indexer_scores", pwork,
+                                                   pk["indexer_scores"], "mfma"),
+                "kernels_us": {k: round(v, 2) for k, v in pk.items()}}}
+    if not args.no_cpu_baseline:
+        n = args.cpu_sample or (8 if wl.mode == "decode" else 32)
+        t0 = time.time()
+        out["cpu_baseline"] = cpu_baseline(wl, n)
+        log(f"cpu baseline in {time.time() - t0:.1f}s")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

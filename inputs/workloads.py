@@ -101,8 +101,10 @@ TINY = Workload(0, "tiny", "tiny", batch=1, n_tokens=12, start_pos=0,
 TINY_DECODE_POSITIONS = (12, 13)
 
 
-def decode_sequence(wl: Workload, b: int) -> dict:
-    """Inputs of one sequence of a decode workload (one new token at start_pos)."""
+def decode_sequence(wl: Workload, b: int, with_ties: bool = True) -> dict:
+    """Inputs of one sequence of a decode workload (one new token at start_pos).
+    with_ties=False returns the long-context workload's keys before the ties
+    are planted."""
     s = wl.seed(b)
     H, D, W = wl.n_heads, wl.head_dim, wl.window
     HI, DI, L = wl.index_heads, wl.index_dim, wl.n_rows
@@ -117,7 +119,7 @@ def decode_sequence(wl: Workload, b: int) -> dict:
         "w": S.uniform_f32(s, S.TAG_W, (1, HI), scale=wl.w_scale),
         "q": S.normal_bf16(s, S.TAG_Q, (1, H, D)),
     }
-    if wl.ties:
+    if wl.ties and with_ties:
         apply_ties(wl, b, d["kI"])
     return d
 
