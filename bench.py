@@ -265,22 +265,38 @@ def run_workload(name, steps, warmup, n_sets, torch, device):
     log(f"{name}: staged {n_sets} input sets in {time.time() - t0:.1f}s")
 
     calls = [step_calls(s, wl.mode) for s in sets]
-    step_graphs = [capture([f for _, f in c], torch) for c in calls]
-    for i in range(warmup):
-        step_graphs[i % n_sets].replay()
+    # One graph holds one step per input set, as one graph would hold the
+    # layers of a model; single-step graphs cover a remainder of K.
+    all_graph = capture([f for c in calls for _, f in c], torch)
+    one_graphs = [capture([f for _, f in c], torch) for c in calls]
+    for i in range(max(1, warmup // n_sets)):
+        all_graph.replay()
     torch.cuda.synchronize()
-    ms_step = time_replays(step_graphs, steps, torch)
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    full, rest = divmod(steps, n_sets)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(full):
+        all_graph.replay()
+    for i in range(rest):
+        one_graphs[i].replay()
+    e1.record(st)
+    e1.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
     log(f"{name}: {ms_step * 1e3:.1f} us per step")
 
-    # per-kernel durations: graphs of one kernel each, replayed over the sets
+    # per-kernel durations: a graph of 4 * n_sets launches of one kernel
+    # cycling over the input sets, replayed; mean time per launch
     kern_us = {}
+    per_graph = 4 * n_sets
     for ki, (kname, _) in enumerate(calls[0]):
-        gs = [capture([c[ki][1]], torch) for c in calls]
-        for i in range(3):
-            gs[i % n_sets].replay()
-        kern_us[kname] = time_replays(gs, max(steps, 20), torch) * 1e3
+        g = capture([calls[i % n_sets][ki][1] for i in range(per_graph)], torch)
+        g.replay()
+        reps = max(4, steps // per_graph)
+        kern_us[kname] = time_replays([g], reps, torch) * 1e3 / per_graph
     # restore a consistent state (the index buffer is rebuilt by a full step)
-    step_graphs[0].replay()
+    one_graphs[0].replay()
     torch.cuda.synchronize()
 
     idx = sets[0].idx.cpu().numpy()
@@ -313,7 +329,7 @@ def roofline_entry(kname, work, us, bound):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=48)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode64", choices=sorted(WL.WORKLOADS))
     ap.add_argument("--input-sets", type=int, default=3)
@@ -361,7 +377,7 @@ def main():
         "kernels_us": {k: round(v, 2) for k, v in kern_us.items()},
     }
     if not args.no_secondary and wl.name != "prefill":
-        pw, pms, pk, pwork = run_workload("prefill", max(10, args.steps // 2), 3,
+        pw, pms, pk, pwork = run_workload("prefill", max(12, args.steps // 2), 3,
                                           args.input_sets, torch, device)
         out["secondary"] = {
             "prefill": {

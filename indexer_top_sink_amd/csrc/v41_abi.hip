@@ -81,6 +81,8 @@ int v41_fp8_round_rows(const v41_bf16* in, int64_t in_ld, v41_bf16* out, int64_t
     return fail(V41_EINVAL, "fp8_round_rows: ring given with ring_slots <= 0");
   if (ring != nullptr && first_pos < 0)
     return fail(V41_EINVAL, "fp8_round_rows: first_pos < 0");
+  if (rows * (int64_t)(row_len / 8) >= 0x7FFFFFFFLL)
+    return fail(V41_EINVAL, "fp8_round_rows: rows * row_len / 8 must stay below 2^31");
   int rc = check_device();
   if (rc) return rc;
   return launched(v41::launch_fp8_round_rows(in, in_ld, out, out_ld, rows, row_len, ring,
@@ -101,6 +103,8 @@ int v41_window_idx(int64_t start_pos, int32_t n_tokens, int32_t window, int32_t 
                                  (long long)idx_ld, cols);
   if (batch > 1 && idx_bs < (int64_t)n_tokens * idx_ld)
     return fail(V41_EINVAL, "window_idx: idx_bs too small");
+  if ((int64_t)batch * n_tokens * cols >= 0x7FFFFFFFLL)
+    return fail(V41_EINVAL, "window_idx: batch * n_tokens * cols must stay below 2^31");
   if (idx == nullptr && (int64_t)batch * n_tokens * cols > 0)
     return fail(V41_EINVAL, "window_idx: NULL idx");
   if (cols_out) *cols_out = cols;
@@ -127,6 +131,7 @@ int v41_indexer_scores(const v41_bf16* qI, const v41_bf16* kI, int64_t kI_bs, co
   if (start_pos > 0 && n_tokens != 1)
     return fail(V41_EINVAL, "indexer_scores: a decode call (start_pos > 0) takes one token");
   if (scores_ld < n_rows) return fail(V41_EINVAL, "indexer_scores: scores_ld < n_rows");
+  if (n_rows >= 0x7FFFFFFFLL) return fail(V41_EINVAL, "indexer_scores: n_rows must stay below 2^31");
   if (batch > 1 && kI_bs < n_rows * head_dim)
     return fail(V41_EINVAL, "indexer_scores: kI_bs < n_rows * head_dim");
   if (kI_bs % 8 != 0) return fail(V41_EINVAL, "indexer_scores: kI_bs must be a multiple of 8");

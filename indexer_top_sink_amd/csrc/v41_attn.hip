@@ -33,6 +33,7 @@ constexpr int kTile = 32;
 constexpr int kHeadsPerBlock = 64;
 constexpr int kMaxWidth = 2048;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleLog2 = 8.0f;  // probabilities stay below 2^8 before a rescale
 
 struct Params {
   const uint16_t* q;
@@ -65,7 +66,7 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 template <int D>
-struct Smem {
+struct alignas(16) Smem {
   static constexpr int kRowStride = D + 8;  // elements; 16 bytes of padding
   static constexpr int kColStride = 40;     // elements; 32 rows + 8 padding
   uint16_t rows[kTile * kRowStride];        // row-major tile
@@ -79,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   constexpr int KS = D / 32;        // QK K-steps
   constexpr int MT = D / 16;        // PV M-tiles (dims)
   constexpr int PAIRS = 4 * (D / 8);  // loader (row group, 16-byte column) pairs
-  __shared__ Smem<D> sm;
+  __shared__ __attribute__((aligned(16))) Smem<D> sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -198,14 +199,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
     if (tile + 1 < t_end) gather(tile + 1);
 
     // S^T tile: rows 16mt + 4g + i, head r16
-    f32x4 sacc[2];
+    f32x4 sacc[2] = {(f32x4){0.f, 0.f, 0.f, 0.f}, (f32x4){0.f, 0.f, 0.f, 0.f}};
+    const uint16_t* rp = &sm.rows[r16 * Smem<D>::kRowStride + 8 * g];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      sacc[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-      const uint16_t* rp = &sm.rows[(16 * mt + r16) * Smem<D>::kRowStride + 8 * g];
+    for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(rp + 32 * kk);
+      for (int mt = 0; mt < 2; ++mt) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(rp + 16 * mt * Smem<D>::kRowStride +
+                                                       32 * kk);
         sacc[mt] = mfma16x16x32(as_bf16x8(a), qf[kk], sacc[mt]);
       }
     }
@@ -223,26 +224,35 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m2, mx);
-    const float alpha = (m_new == m2) ? 1.0f : exp2f(m2 - m_new);
-    m2 = m_new;
+    // Lazy rescaling: probabilities are taken relative to a reference max m2
+    // that only moves when a score exceeds it by more than 2^8 (O and l share
+    // the reference, so the final O / l is unchanged); the branch is uniform
+    // across the wavefront.
+    if (__any(mx > m2 + kRescaleLog2)) {
+      const float m_new = fmaxf(m2, mx);
+      const float alpha = (m_new == m2) ? 1.0f : exp2f(m2 - m_new);
+      m2 = m_new;
+      l_part *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc_o[mt] *= alpha;
+    }
     u32x4 pk;
     float psum = 0.0f;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float p0 = (sv[2 * j] == kNegInf) ? 0.0f : exp2f(sv[2 * j] - m_new);
-      const float p1 = (sv[2 * j + 1] == kNegInf) ? 0.0f : exp2f(sv[2 * j + 1] - m_new);
+      const float p0 = (sv[2 * j] == kNegInf) ? 0.0f : exp2f(sv[2 * j] - m2);
+      const float p1 = (sv[2 * j + 1] == kNegInf) ? 0.0f : exp2f(sv[2 * j + 1] - m2);
       psum += p0 + p1;
       pk[j] = f32_to_bf16_bits(p0) | (f32_to_bf16_bits(p1) << 16);
     }
-    l_part = l_part * alpha + psum;
+    l_part += psum;
     const bf16x8 pf = as_bf16x8(pk);
     // O^T += G^T P^T
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const u32x4 a = *reinterpret_cast<const u32x4*>(
           &sm.cols[(16 * mt + r16) * Smem<D>::kColStride + 8 * g]);
-      acc_o[mt] = mfma16x16x32(as_bf16x8(a), pf, acc_o[mt] * alpha);
+      acc_o[mt] = mfma16x16x32(as_bf16x8(a), pf, acc_o[mt]);
     }
     lds_barrier();
   }

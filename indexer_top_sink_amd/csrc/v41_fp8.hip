@@ -34,18 +34,19 @@ __device__ __forceinline__ uint32_t round_one(uint32_t xb, float inv_s, float s)
 
 __global__ __launch_bounds__(kThreads) void fp8_round_rows_kernel(
     const uint16_t* __restrict__ in, int64_t in_ld, uint16_t* out, int64_t out_ld,
-    int64_t rows, int32_t chunks_per_row, int32_t row_len, uint16_t* ring,
-    int32_t ring_slots, int64_t first_pos, int64_t ring_first_row) {
-  const int64_t total = rows * chunks_per_row;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-       g - (threadIdx.x & 3) < total; g += stride) {
+    int32_t rows, int32_t chunks_per_row, int32_t row_len, uint16_t* ring,
+    int32_t ring_slots, int64_t first_pos, int32_t ring_first_row) {
+  // the C ABI keeps rows * chunks_per_row below 2^31
+  const int32_t total = rows * chunks_per_row;
+  const int32_t stride = (int32_t)gridDim.x * kThreads;
+  for (int32_t g = (int32_t)blockIdx.x * kThreads + (int32_t)threadIdx.x;
+       g - (int32_t)(threadIdx.x & 3) < total; g += stride) {
     // total is a multiple of 4, so the four lanes of a block agree on `live`
     const bool live = g < total;
-    const int64_t r = live ? g / chunks_per_row : 0;
-    const int32_t c = live ? (int32_t)(g - r * chunks_per_row) : 0;
+    const int32_t r = live ? g / chunks_per_row : 0;
+    const int32_t c = live ? g - r * chunks_per_row : 0;
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (live) v = *reinterpret_cast<const u32x4*>(in + r * in_ld + (int64_t)c * 8);
+    if (live) v = *reinterpret_cast<const u32x4*>(in + (int64_t)r * in_ld + c * 8);
     // |x| bit patterns compare like magnitudes for finite values
     uint32_t m = 0;
 #pragma unroll
@@ -69,10 +70,10 @@ __global__ __launch_bounds__(kThreads) void fp8_round_rows_kernel(
       o[i] = lo | (hi << 16);
     }
     if (live) {
-      *reinterpret_cast<u32x4*>(out + r * out_ld + (int64_t)c * 8) = o;
+      *reinterpret_cast<u32x4*>(out + (int64_t)r * out_ld + c * 8) = o;
       if (ring != nullptr && r >= ring_first_row) {
-        int64_t slot = (first_pos + r) % ring_slots;
-        *reinterpret_cast<u32x4*>(ring + slot * row_len + (int64_t)c * 8) = o;
+        const int64_t slot = (first_pos + r) % ring_slots;
+        *reinterpret_cast<u32x4*>(ring + slot * row_len + c * 8) = o;
       }
     }
   }
@@ -91,8 +92,8 @@ hipError_t launch_fp8_round_rows(const uint16_t* in, int64_t in_ld, uint16_t* ou
   if (blocks > 65536) blocks = 65536;
   const int64_t ring_first = ring ? (rows > ring_slots ? rows - ring_slots : 0) : rows;
   hipLaunchKernelGGL(fp8_round_rows_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s,
-                     in, in_ld, out, out_ld, rows, cpr, row_len, ring, ring_slots,
-                     first_pos, ring_first);
+                     in, in_ld, out, out_ld, (int32_t)rows, cpr, row_len, ring, ring_slots,
+                     first_pos, (int32_t)ring_first);
   return hipGetLastError();
 }
 

@@ -74,8 +74,9 @@ __global__ __launch_bounds__(256) void indexer_kernel(
   const uint16_t* __restrict__ kb = kI + b * kI_bs + 8 * g;
   const uint8_t* __restrict__ crow = cand ? cand + q * cand_width : nullptr;
 
+  // positions stay below 2^31 (checked by the C ABI), so 32-bit division
   auto allowed = [&](int64_t j) -> bool {
-    return j < live_end && (crow == nullptr || crow[j / cand_block] != 0);
+    return j < live_end && (crow == nullptr || crow[(uint32_t)j / (uint32_t)cand_block] != 0);
   };
   auto load_block = [&](int64_t j0, u32x4 (&buf)[KS]) {
     const int64_t j = j0 + r16;

@@ -59,7 +59,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* scratc
 
 template <int NT, int CAP>
 __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scores,
-                                                  int64_t n_cols, int64_t scores_ld, int32_t k,
+                                                  int32_t n_cols, int64_t scores_ld, int32_t k,
                                                   int32_t offset, int32_t* __restrict__ idx,
                                                   int64_t idx_ld) {
   __shared__ uint32_t keys[CAP > 0 ? CAP : 1];
@@ -76,13 +76,13 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
   int32_t* __restrict__ orow = idx + row * idx_ld;
   const bool staged = n_cols <= CAP;
 
-  auto key_at = [&](int64_t j) -> uint32_t {
+  auto key_at = [&](int32_t j) -> uint32_t {
     return staged ? keys[j] : score_key(srow[j]);
   };
 
   // 1. keys and the count of selectable positions
   uint32_t nv_t = 0;
-  for (int64_t j = tid; j < n_cols; j += NT) {
+  for (int32_t j = tid; j < n_cols; j += NT) {
     const uint32_t kk = score_key(srow[j]);
     if (staged) keys[j] = kk;
     nv_t += kk != 0u;
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
       for (int i = tid; i < kHistCopies * 256; i += NT) (&hist[0][0])[i] = 0u;
       __syncthreads();
       uint32_t* myhist = hist[lane % kHistCopies];
-      for (int64_t j = tid; j < n_cols; j += NT) {
+      for (int32_t j = tid; j < n_cols; j += NT) {
         const uint32_t kk = key_at(j);
         if (kk != 0u && (kk & pmask) == prefix) atomicAdd(&myhist[(kk >> shift) & 255u], 1u);
       }
@@ -153,13 +153,15 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
   const uint32_t n_gt = m - need;
 
   // 3. contiguous range per thread: count, scan, emit
-  const int64_t C = (n_cols + NT - 1) / NT;
-  const int64_t lo = (int64_t)tid * C;
-  const int64_t hi = lo + C < n_cols ? lo + C : n_cols;
+  const int32_t C = (n_cols + NT - 1) / NT;
+  const int32_t lo = tid * C;
+  const int32_t hi = lo + C < n_cols ? lo + C : n_cols;
   uint32_t cgt = 0, ceq = 0;
-  for (int64_t i = 0; i < C; ++i) {
-    // rotated start spreads the lanes of a wavefront over the LDS banks
-    const int64_t j = lo + (i + tid) % C;
+  // rotated start spreads the lanes of a wavefront over the LDS banks
+  int32_t rot = (C > 0) ? tid % C : 0;
+  for (int32_t i = 0; i < C; ++i) {
+    const int32_t j = lo + rot;
+    rot = (rot + 1 == C) ? 0 : rot + 1;
     if (j < hi) {
       const uint32_t kk = key_at(j);
       cgt += kk > T;
@@ -169,7 +171,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
   uint32_t tot_gt, tot_eq;
   uint32_t at_gt = block_excl_scan<NT>(cgt, scratch, tot_gt);
   uint32_t at_eq = block_excl_scan<NT>(ceq, scratch, tot_eq);
-  for (int64_t j = lo; j < hi; ++j) {
+  for (int32_t j = lo; j < hi; ++j) {
     const uint32_t kk = key_at(j);
     const unsigned long long comp =
         ((unsigned long long)kk << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)j);
@@ -181,13 +183,23 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     }
   }
 
-  // 4. bitonic sort of sel[0 .. P) descending, P = next power of two >= m
+  // 4. bitonic sort of sel[0 .. P) descending, P = next power of two >= m.
+  // Pair i of a stage is handled by thread i mod NT, so a wavefront owns the
+  // 128-element chunks of its pairs; stages whose stride stays inside a chunk
+  // (<= 64) need only the in-order LDS accesses of one wavefront, and a block
+  // barrier is placed only next to stages that cross chunks.
   uint32_t P = 1;
   while (P < m) P <<= 1;
   for (uint32_t i = m + tid; i < P; i += NT) sel[i] = 0ull;
   __syncthreads();
+  uint32_t prev_stride = 0;
   for (uint32_t size = 2; size <= P; size <<= 1) {
     for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+      if (stride >= 128 || prev_stride >= 128)
+        __syncthreads();
+      else
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      prev_stride = stride;
       for (uint32_t i = tid; i < P / 2; i += NT) {
         const uint32_t a = 2 * i - (i & (stride - 1));
         const uint32_t b = a + stride;
@@ -198,9 +210,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
           sel[b] = x;
         }
       }
-      __syncthreads();
     }
   }
+  __syncthreads();
 
   // 5. positions + offset, then -1
   for (int32_t i = tid; i < k; i += NT) {
@@ -217,14 +229,15 @@ hipError_t launch_topk_select(const float* scores, int64_t n_sel_rows, int64_t n
                               int64_t idx_ld, hipStream_t s) {
   if (n_sel_rows == 0) return hipSuccess;
   const dim3 grid((unsigned)n_sel_rows);
+  const int32_t nc = (int32_t)n_cols;  // the ABI bounds n_cols below 2^31
   if (n_cols <= 4096) {
-    hipLaunchKernelGGL((topk_kernel<256, 4096>), grid, dim3(256), 0, s, scores, n_cols,
+    hipLaunchKernelGGL((topk_kernel<256, 4096>), grid, dim3(256), 0, s, scores, nc,
                        scores_ld, k, offset, idx, idx_ld);
   } else if (n_cols <= 32768) {
-    hipLaunchKernelGGL((topk_kernel<1024, 32768>), grid, dim3(1024), 0, s, scores, n_cols,
+    hipLaunchKernelGGL((topk_kernel<1024, 32768>), grid, dim3(1024), 0, s, scores, nc,
                        scores_ld, k, offset, idx, idx_ld);
   } else {
-    hipLaunchKernelGGL((topk_kernel<1024, 0>), grid, dim3(1024), 0, s, scores, n_cols,
+    hipLaunchKernelGGL((topk_kernel<1024, 0>), grid, dim3(1024), 0, s, scores, nc,
                        scores_ld, k, offset, idx, idx_ld);
   }
   return hipGetLastError();

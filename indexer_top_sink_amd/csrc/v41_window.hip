@@ -11,14 +11,15 @@ __global__ __launch_bounds__(256) void window_idx_kernel(int64_t start_pos, int3
                                                          int32_t window, int32_t cols,
                                                          int32_t batch, int32_t* idx,
                                                          int64_t idx_ld, int64_t idx_bs) {
-  const int64_t per_seq = (int64_t)n_tokens * cols;
-  const int64_t total = per_seq * batch;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t b = e / per_seq;
-    const int64_t rem = e - b * per_seq;
-    const int32_t t = (int32_t)(rem / cols);
-    const int32_t c = (int32_t)(rem - (int64_t)t * cols);
+  // the C ABI keeps batch * n_tokens * cols below 2^31
+  const int32_t per_seq = n_tokens * cols;
+  const int32_t total = per_seq * batch;
+  for (int32_t e = (int32_t)(blockIdx.x * blockDim.x + threadIdx.x); e < total;
+       e += (int32_t)(gridDim.x * blockDim.x)) {
+    const int32_t b = e / per_seq;
+    const int32_t rem = e - b * per_seq;
+    const int32_t t = rem / cols;
+    const int32_t c = rem - t * cols;
     int32_t v;
     if (start_pos == 0) {
       // causal band of the chunk: rows max(0, t-window+1) .. t, then -1
@@ -30,7 +31,7 @@ __global__ __launch_bounds__(256) void window_idx_kernel(int64_t start_pos, int3
     } else {
       v = (c <= start_pos) ? c : -1;
     }
-    idx[b * idx_bs + (int64_t)t * idx_ld + c] = v;
+    idx[(int64_t)b * idx_bs + (int64_t)t * idx_ld + c] = v;
   }
 }
 
