@@ -136,9 +136,10 @@ int v41_indexer_scores(const v41_bf16 *qI, const v41_bf16 *kI, int64_t kI_bs,
  * the window rows and -1 marks an absent entry).
  *
  * Per score row: valid positions are those whose score is neither -inf nor
- * NaN.  The m = min(k, #valid) best are written as position + offset, in
- * order of score descending then position ascending (equal scores, with +0
- * equal to -0, go to the lower position), followed by -1 up to k entries.
+ * NaN.  The m = min(k, #valid) best (ranked by score descending; equal
+ * scores, with +0 equal to -0, go to the lower position) form the selection,
+ * a set, written as position + offset in ascending position order and
+ * followed by -1 up to k entries.
  *
  *   scores  f32 [n_sel_rows][scores_ld], n_cols <= scores_ld
  *   idx     int32 [n_sel_rows][idx_ld]; entries 0 .. k-1 of each row are

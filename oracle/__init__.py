@@ -166,7 +166,8 @@ def indexer_scores(qI: np.ndarray, kI: np.ndarray, w: np.ndarray, start_pos: int
 # ---------------------------------------------------------------- top-k
 def topk(scores: np.ndarray, k: int, offset: int = 0) -> np.ndarray:
     """scores [R, L] (any float dtype; converted exactly to double) ->
-    int32 [R, k]: positions + offset in (score desc, position asc) order, -1 pad."""
+    int32 [R, k]: the selected positions + offset in ascending position order
+    (the selection ranks by score desc, then position asc), -1 pad."""
     s = _c(np.asarray(scores, dtype=np.float64), np.float64)
     R, L = s.shape
     out = np.empty((R, k), dtype=np.int32)

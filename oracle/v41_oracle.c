@@ -29,7 +29,8 @@
  *  - A negative value that rounds to zero keeps its sign (-0).
  *  - The top-k breaks ties by the lower position; +0 and -0 are equal;
  *    -inf and NaN scores are excluded; fewer than k valid positions are
- *    padded with -1.  The output is in (score desc, position asc) order.
+ *    padded with -1.  The selection is a set; it is written in ascending
+ *    position order.
  *  - The softmax subtracts m = max(sink_h, max_i s_i) before exp: the
  *    result is the same real number, it only avoids overflow of exp.
  *  - Index values outside [0, rows_a_len + rows_b_len) are skipped like -1.
@@ -292,11 +293,18 @@ static int cmp_scored(const void *pa, const void *pb)
     return 0;
 }
 
+static int cmp_position(const void *pa, const void *pb)
+{
+    int64_t a = ((const struct ora_scored *)pa)->j;
+    int64_t b = ((const struct ora_scored *)pb)->j;
+    return (a > b) - (a < b);
+}
+
 /*
- * Valid positions are those whose score is neither -inf nor NaN.  Writes the
- * m = min(k, #valid) best positions plus offset, in (score desc, position
- * asc) order, then -1 up to k entries.  Returns m, or -1 on allocation
- * failure.
+ * Valid positions are those whose score is neither -inf nor NaN.  The m =
+ * min(k, #valid) best positions in (score desc, position asc) order form the
+ * selection; it is written as positions plus offset in ascending position
+ * order, then -1 up to k entries.  Returns m, or -1 on allocation failure.
  */
 int64_t ora_topk_one(const double *scores, int64_t n, int32_t k,
                      int32_t offset, int32_t *out)
@@ -316,6 +324,7 @@ int64_t ora_topk_one(const double *scores, int64_t n, int32_t k,
     }
     qsort(v, (size_t)nv, sizeof(struct ora_scored), cmp_scored);
     int64_t m = nv < k ? nv : k;
+    qsort(v, (size_t)m, sizeof(struct ora_scored), cmp_position);
     for (int32_t i = 0; i < k; ++i)
         out[i] = (i < m) ? (int32_t)(v[i].j + offset) : -1;
     free(v);
