@@ -8,21 +8,24 @@
 // rows through LDS in tiles of 32:
 //  * the idx row is compacted first (entries outside the two row sources are
 //    dropped), so -1 padding costs neither loads nor matrix-core time;
-//  * gather: each thread loads 16 contiguous bytes from each of 8 rows (a
-//    load instruction covers 4 rows x 256 contiguous bytes), one tile ahead
-//    of the tile being multiplied; it stores them row-major and, after an 8x8
-//    transpose of 16-bit values in registers, dimension-major;
+//  * gather: rows go from HBM straight into LDS with global_load_lds_dwordx4
+//    (one 1 KB row per wavefront instruction, row address in scalar
+//    registers), into a double buffer one tile ahead of the tile in use;
+//    16-byte chunks are xor-swizzled by row so the reads below hit distinct
+//    LDS banks;
 //  * S^T = G Q^T on the matrix cores (v_mfma_f32_16x16x32_bf16): A operand =
-//    16 rows x 32 dims from the row-major copy, B operand = the wave's query
+//    16 rows x 32 dims read with ds_read_b128, B operand = the wave's query
 //    fragments held in registers;
-//  * online softmax in f32 on the log2 scale; the running max starts at the
-//    sink, which enters only the final denominator;
-//  * O^T += G^T P^T: A operand = 16 dims x 32 rows from the dimension-major
-//    copy, B operand = the probabilities exactly as the S^T accumulator left
-//    them in the lane (the tile's rows are stored in the order that makes the
-//    accumulator layout the operand layout), rounded to bf16.
-// A query's rows may be split over several workgroups (decode: few queries);
-// each writes an f32 partial (max, sum, O) and a combine kernel merges them.
+//  * online softmax in f32 on the log2 scale; the reference max starts at the
+//    sink (which enters only the final denominator) and is moved lazily;
+//  * O^T += G^T P^T: the A operand (16 dims x 32 rows) comes from the same
+//    row-major tile through two ds_read_b64_tr_b16 transposing loads, and the
+//    B operand is the probabilities exactly as the S^T accumulator left them
+//    in the lane (the transposing loads fetch the rows in that order), rounded
+//    to bf16.
+// Decode has few queries: a query's rows are then split over several
+// workgroups, each writing an f32 partial (max, sum, O), and a combine kernel
+// merges them.
 #include "v41_common.h"
 
 namespace v41 {
@@ -34,6 +37,8 @@ constexpr int kHeadsPerBlock = 64;
 constexpr int kMaxWidth = 2048;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleLog2 = 8.0f;  // probabilities stay below 2^8 before a rescale
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 struct Params {
   const uint16_t* q;
@@ -53,12 +58,44 @@ struct Params {
   int32_t splits;
 };
 
-// Tile row held by loader group rg (0..3), slot s (0..7).  Rows 0..15 form
-// the first 16-row MFMA tile and rows 16..31 the second; slot s < 4 is row
-// 4 rg + s and slot s >= 4 is row 16 + 4 rg + s - 4, which is where the S^T
-// accumulator of lane group rg keeps them.
-__device__ __forceinline__ int tile_row(int rg, int s) {
-  return (s < 4) ? 4 * rg + s : 16 + 4 * rg + (s - 4);
+// LDS placement of a 32-row tile.  A wavefront load instruction fills one
+// 1 KB block (RPI rows of D values); blocks are padded by 32 bytes.  For
+// D = 512 the 16-byte chunk c of row r sits at chunk c ^ ((r >> 3) & 1).
+template <int D>
+struct Tile {
+  static constexpr int LPR = D / 8;      // 16-byte chunks per row
+  static constexpr int RPI = 64 / LPR;   // rows per load instruction
+  static constexpr int kBlkBytes = 1024 + 32;
+  static constexpr int kBlocks = kTile / RPI;
+  static constexpr int kBufBytes = kBlocks * kBlkBytes;
+  static __device__ __forceinline__ int row_off(int r) {
+    return (r / RPI) * kBlkBytes + (r % RPI) * (2 * D);
+  }
+  static __device__ __forceinline__ int swz(int r) { return D == 512 ? ((r >> 3) & 1) : 0; }
+};
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Eight ds_read_b64_tr_b16 (four 16-dim M-tiles, rows of slots 0..3 and
+// 4..7) and a wait for them.  Written as one asm block so the compiler does
+// not make these LDS reads wait for the direct-to-LDS loads of the next tile,
+// which target the other buffer.
+__device__ __forceinline__ void tr_load4(u32x2 (&t)[8], uint32_t lo, uint32_t hi) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %8 offset:32\n\t"
+      "ds_read_b64_tr_b16 %3, %9 offset:32\n\t"
+      "ds_read_b64_tr_b16 %4, %8 offset:64\n\t"
+      "ds_read_b64_tr_b16 %5, %9 offset:64\n\t"
+      "ds_read_b64_tr_b16 %6, %8 offset:96\n\t"
+      "ds_read_b64_tr_b16 %7, %9 offset:96\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]),
+        "=&v"(t[6]),
+        "=&v"(t[7])
+      : "v"(lo), "v"(hi)
+      : "memory");
 }
 
 __device__ __forceinline__ void lds_barrier() {
@@ -66,21 +103,13 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 template <int D>
-struct alignas(16) Smem {
-  static constexpr int kRowStride = D + 8;  // elements; 16 bytes of padding
-  static constexpr int kColStride = 40;     // elements; 32 rows + 8 padding
-  uint16_t rows[kTile * kRowStride];        // row-major tile
-  uint16_t cols[D * kColStride];            // dimension-major tile
-  int32_t list[kMaxWidth];                  // compacted joint indices
-  uint32_t wave_cnt[kThreads / kWave];
-};
-
-template <int D>
-__global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
-  constexpr int KS = D / 32;        // QK K-steps
-  constexpr int MT = D / 16;        // PV M-tiles (dims)
-  constexpr int PAIRS = 4 * (D / 8);  // loader (row group, 16-byte column) pairs
-  __shared__ __attribute__((aligned(16))) Smem<D> sm;
+__global__ __launch_bounds__(kThreads, 2) void attn_kernel(Params p) {
+  using TL = Tile<D>;
+  constexpr int KS = D / 32;  // QK K-steps
+  constexpr int MT = D / 16;  // PV M-tiles (dims)
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[2 * TL::kBufBytes];
+  __shared__ int32_t list[kMaxWidth];
+  __shared__ uint32_t wave_cnt[kThreads / kWave];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -108,27 +137,49 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
       const bool ok = ix >= 0 && (int64_t)ix < total_rows;
       cnt += __popcll(__ballot(ok));
     }
-    if (lane == 0) sm.wave_cnt[wave] = cnt;
+    if (lane == 0) wave_cnt[wave] = cnt;
     __syncthreads();
     uint32_t base = 0;
-    for (int w = 0; w < wave; ++w) base += sm.wave_cnt[w];
+    for (int w = 0; w < wave; ++w) base += wave_cnt[w];
     for (int i0 = w0; i0 < w1; i0 += kWave) {
       const int i = i0 + lane;
       const int32_t ix = (i < w1) ? irow[i] : -1;
       const bool ok = ix >= 0 && (int64_t)ix < total_rows;
       const unsigned long long bal = __ballot(ok);
       const uint32_t before = __popcll(bal & ((1ull << lane) - 1ull));
-      if (ok) sm.list[base + before] = ix;
+      if (ok) list[base + before] = ix;
       base += __popcll(bal);
     }
   }
   __syncthreads();
   uint32_t n_valid = 0;
-  for (int w = 0; w < kThreads / kWave; ++w) n_valid += sm.wave_cnt[w];
+  for (int w = 0; w < kThreads / kWave; ++w) n_valid += wave_cnt[w];
   const int n_tiles = (int)((n_valid + kTile - 1) / kTile);
   const int tps = (n_tiles + p.splits - 1) / p.splits;
   const int t_begin = split * tps;
   const int t_end = (t_begin + tps < n_tiles) ? t_begin + tps : n_tiles;
+
+  // ---- gather of one tile into LDS buffer `buf` (rows past n_valid repeat
+  // the first valid row: finite data whose probability is 0)
+  const uint16_t* a_base = p.rows_a + b * p.a_bs;
+  const uint16_t* b_base = p.rows_b + b * p.b_bs;
+  auto gather = [&](int tile, int buf) {
+    const int base_pos = tile * kTile;
+#pragma unroll
+    for (int bk = wave; bk < TL::kBlocks; bk += kThreads / kWave) {
+      const int r = bk * TL::RPI + lane / TL::LPR;
+      const int c = (lane % TL::LPR) ^ TL::swz(r);
+      int pos = base_pos + r;
+      if ((uint32_t)pos >= n_valid) pos = 0;
+      int64_t ix = list[pos];
+      if (TL::RPI == 1) ix = __builtin_amdgcn_readfirstlane((int)ix);
+      const uint16_t* src = (ix < p.rows_a_len) ? a_base + ix * D
+                                                : b_base + (ix - p.rows_a_len) * D;
+      __builtin_amdgcn_global_load_lds(
+          src + 8 * c, (lds_void*)(size_t)(tiles + buf * TL::kBufBytes + bk * TL::kBlkBytes),
+          16, 0, 0);
+    }
+  };
 
   // ---- query fragments (B operand of S^T = G Q^T): head r16, dims 32kk+8g..
   bf16x8 qf[KS];
@@ -143,70 +194,42 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
   }
   const float sink2 = head_ok ? p.sink[head] * kLog2e : 0.0f;
   const float kNegInf = -__builtin_huge_valf();
-  float m2 = sink2;  // running max on the log2 scale
+  float m2 = sink2;  // reference max on the log2 scale
   float l_part = 0.0f;
   f32x4 acc_o[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc_o[mt] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  // ---- loader
-  const bool loader = tid < PAIRS;
-  const int rg = tid & 3;
-  const int cc = tid >> 2;  // 16-byte column
-  u32x4 stage[8];
-  auto gather = [&](int tile) {
-    if (!loader) return;
-    const int base = tile * kTile;
+  // per-lane LDS byte offsets inside a tile buffer
+  //  QK: row 16mt + r16, chunk 4kk + g (swizzled)
+  int qk_off[2];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const int pos = base + tile_row(rg, s);
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if ((uint32_t)pos < n_valid) {
-        const int64_t ix = sm.list[pos];
-        const uint16_t* src = (ix < p.rows_a_len)
-                                  ? p.rows_a + b * p.a_bs + ix * D
-                                  : p.rows_b + b * p.b_bs + (ix - p.rows_a_len) * D;
-        v = *reinterpret_cast<const u32x4*>(src + 8 * cc);
-      }
-      stage[s] = v;
-    }
-  };
-  auto stash = [&]() {
-    if (!loader) return;
-#pragma unroll
-    for (int s = 0; s < 8; ++s)
-      *reinterpret_cast<u32x4*>(&sm.rows[tile_row(rg, s) * Smem<D>::kRowStride + 8 * cc]) =
-          stage[s];
-    // 8x8 transpose of 16-bit values: column i of the 8 staged rows becomes
-    // dimension 8cc+i, rows in slot order s = 0..7 (positions 8rg .. 8rg+7)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      u32x4 t;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t x = stage[2 * j][i >> 1];
-        const uint32_t y = stage[2 * j + 1][i >> 1];
-        t[j] = (i & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
-      }
-      *reinterpret_cast<u32x4*>(&sm.cols[(8 * cc + i) * Smem<D>::kColStride + 8 * rg]) = t;
-    }
-  };
+  for (int mt = 0; mt < 2; ++mt) {
+    const int r = 16 * mt + r16;
+    qk_off[mt] = TL::row_off(r) + 16 * (g ^ TL::swz(r));
+  }
+  //  PV transposing loads: lane (g, a, bb) reads 8 bytes of row 4g + a (first)
+  //  and 16 + 4g + a (second) at dims 16mt + 4bb
+  const int ta = (lane >> 2) & 3, tb = lane & 3;
+  const int r_lo = 4 * g + ta, r_hi = 16 + 4 * g + ta;
+  const int tr_lo = TL::row_off(r_lo) + 16 * ((tb >> 1) ^ TL::swz(r_lo)) + 8 * (tb & 1);
+  const int tr_hi = TL::row_off(r_hi) + 16 * ((tb >> 1) ^ TL::swz(r_hi)) + 8 * (tb & 1);
 
-  if (t_begin < t_end) gather(t_begin);
+  if (t_begin < t_end) gather(t_begin, 0);
   for (int tile = t_begin; tile < t_end; ++tile) {
-    stash();
+    const int buf = (tile - t_begin) & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
-    if (tile + 1 < t_end) gather(tile + 1);
+    if (tile + 1 < t_end) gather(tile + 1, buf ^ 1);
+    const uint8_t* tb_base = tiles + buf * TL::kBufBytes;
 
     // S^T tile: rows 16mt + 4g + i, head r16
     f32x4 sacc[2] = {(f32x4){0.f, 0.f, 0.f, 0.f}, (f32x4){0.f, 0.f, 0.f, 0.f}};
-    const uint16_t* rp = &sm.rows[r16 * Smem<D>::kRowStride + 8 * g];
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(rp + 16 * mt * Smem<D>::kRowStride +
-                                                       32 * kk);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(tb_base + qk_off[mt] + 64 * kk);
         sacc[mt] = mfma16x16x32(as_bf16x8(a), qf[kk], sacc[mt]);
       }
     }
@@ -224,10 +247,9 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // Lazy rescaling: probabilities are taken relative to a reference max m2
-    // that only moves when a score exceeds it by more than 2^8 (O and l share
-    // the reference, so the final O / l is unchanged); the branch is uniform
-    // across the wavefront.
+    // lazy rescale: the reference moves only when a score exceeds it by more
+    // than 2^8 (O and l share the reference, so O / l is unchanged); the
+    // branch is uniform across the wavefront
     if (__any(mx > m2 + kRescaleLog2)) {
       const float m_new = fmaxf(m2, mx);
       const float alpha = (m_new == m2) ? 1.0f : exp2f(m2 - m_new);
@@ -236,25 +258,28 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(Params p) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc_o[mt] *= alpha;
     }
-    u32x4 pk;
+    bf16x8 pf;
     float psum = 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float p0 = (sv[2 * j] == kNegInf) ? 0.0f : exp2f(sv[2 * j] - m2);
-      const float p1 = (sv[2 * j + 1] == kNegInf) ? 0.0f : exp2f(sv[2 * j + 1] - m2);
-      psum += p0 + p1;
-      pk[j] = f32_to_bf16_bits(p0) | (f32_to_bf16_bits(p1) << 16);
+    for (int s = 0; s < 8; ++s) {
+      const float pv = (sv[s] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(sv[s] - m2);
+      psum += pv;
+      pf[s] = (__bf16)pv;
     }
     l_part += psum;
-    const bf16x8 pf = as_bf16x8(pk);
-    // O^T += G^T P^T
+    // O^T += G^T P^T, four M-tiles per batch of transposing loads
+    const uint32_t lds_lo = (uint32_t)(size_t)(tb_base + tr_lo);
+    const uint32_t lds_hi = (uint32_t)(size_t)(tb_base + tr_hi);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(
-          &sm.cols[(16 * mt + r16) * Smem<D>::kColStride + 8 * g]);
-      acc_o[mt] = mfma16x16x32(as_bf16x8(a), pf, acc_o[mt]);
+    for (int mt0 = 0; mt0 < MT; mt0 += 4) {
+      u32x2 t[8];
+      tr_load4(t, lds_lo + 32 * mt0, lds_hi + 32 * mt0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 a = {t[2 * j][0], t[2 * j][1], t[2 * j + 1][0], t[2 * j + 1][1]};
+        acc_o[mt0 + j] = mfma16x16x32(as_bf16x8(a), pf, acc_o[mt0 + j]);
+      }
     }
-    lds_barrier();
   }
 
   // ---- epilogue: lane holds O^T[dims 16mt + 4g + i][head r16]
