@@ -4,131 +4,249 @@
 //
 // The contraction is qI[heads x DI] x kI^T[DI x 16 positions] on the matrix
 // cores (v_mfma_f32_16x16x32_bf16): the heads are the M side (16 per tile, up
-// to 4 tiles), 16 positions the N side, DI the K side.  One wavefront owns a
-// query and a run of positions: its qI fragments and weights stay in
-// registers, and it streams the index keys straight from HBM into MFMA B
-// operands (each lane loads 16 contiguous bytes of one key; the 16-lane groups
-// of a load cover 16 keys x 64 bytes), one 16-key block ahead of the block it
-// multiplies.  The epilogue applies ReLU and the weights in f32, sums the 4
-// heads a lane holds per tile, then across the 4 lane groups with two
-// xor-shuffles.  Keys past the causal bound or in a masked candidate block are
-// never loaded; their scores are -inf.
+// to 4 tiles), 16 positions the N side, DI the K side.
+//
+// A workgroup of four wavefronts owns one query and a share of its positions.
+// The query's qI (at most 64 x 128 bf16) and weights go through LDS once per
+// workgroup and then sit in registers.  The positions are cut into 16-key
+// blocks dealt round-robin to the query's wavefronts, so neighbouring
+// wavefronts stream neighbouring 4 KB blocks.  Each wavefront keeps a private
+// ring of kStages blocks in LDS, filled by global_load_lds_dwordx4: every
+// instruction moves 1 KB of contiguous key bytes (the access pattern HBM
+// streams best), and the lanes permute 16-byte chunks within each key row so
+// that the MFMA operand reads from LDS hit distinct banks.  The wavefront
+// waits on the oldest block with an explicit vmcnt, reads it, refills the slot
+// with the block kStages ahead, and multiplies.
+//
+// The epilogue applies ReLU and the weights in f32, sums the 4 heads a lane
+// holds per tile, then across the 4 lane groups with two xor-shuffles.  Keys
+// past the causal bound are never loaded and score -inf; with a candidate mask
+// a last pass overwrites the masked positions with -inf (their products were
+// computed and are discarded).
 #include "v41_common.h"
 
 namespace v41 {
 namespace {
 
-constexpr int kWavesPerBlock = 4;
+typedef __attribute__((address_space(3))) void lds_void;
 
-template <int DI, int HT>
-__global__ __launch_bounds__(256) void indexer_kernel(
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kStages = 2;
+
+template <int DI>
+struct KeyTile {
+  static constexpr int KS = DI / 32;         // MFMA k-steps = 1 KB loads per block
+  static constexpr int CPR = DI / 8;         // 16-byte chunks in a key row
+  static constexpr int kBytes = 16 * DI * 2; // one 16-key block
+  // Chunk c of row r sits in slot c ^ swz(r) of that row.  Rows 256 bytes
+  // apart (or two or four to 256 bytes) get different permutations, so the
+  // 16 rows a ds_read_b128 touches spread over all banks.
+  static __device__ __forceinline__ int swz(int r) { return (r / (16 / CPR)) & (CPR - 1); }
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// KS ds_read_b128 and a wait for them, as one asm block: the compiler neither
+// reorders the uses above the wait nor makes these reads wait for the
+// direct-to-LDS loads still in flight into the other ring slots.
+template <int KS>
+__device__ __forceinline__ void lds_read_ks(u32x4 (&o)[KS], const uint32_t (&a)[KS], uint32_t base) {
+  if constexpr (KS == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+        : "v"(a[0] + base), "v"(a[1] + base), "v"(a[2] + base), "v"(a[3] + base)
+        : "memory");
+  } else if constexpr (KS == 2) {
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o[0]), "=&v"(o[1])
+        : "v"(a[0] + base), "v"(a[1] + base)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %1\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(o[0])
+        : "v"(a[0] + base)
+        : "memory");
+  }
+}
+
+// One 16-key block, rows j0 .. j0+15, into a ring slot: KS loads of 1 KB
+// each (LDS byte 1024 c + 16 lane of the slot).  Rows at or past live_end
+// reload row j0 (j0 < live_end keeps every address inside the keys).
+template <int DI, int AUX>
+__device__ __forceinline__ void issue_block(const uint16_t* kb, int j0, int live_end, int lane,
+                                            uint8_t* slot) {
+  using KT = KeyTile<DI>;
+#pragma unroll
+  for (int c = 0; c < KT::KS; ++c) {
+    const int s = 64 * c + lane;
+    const int r = s / KT::CPR;
+    const int pos = s % KT::CPR;
+    int j = j0 + r;
+    if (j >= live_end) j = j0;
+    const uint16_t* src = kb + (int64_t)j * DI + 8 * (pos ^ KT::swz(r));
+    lds_void* dst = (lds_void*)(size_t)(slot + 1024 * c);
+    // the cache-policy operand must be a literal for the host pass
+    if constexpr (AUX == 2) __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 2);
+    else __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+  }
+}
+
+template <int DI, int HT, int NT>
+__global__ __launch_bounds__(kThreads, 2) void indexer_kernel(
     const uint16_t* __restrict__ qI, const uint16_t* __restrict__ kI, int64_t kI_bs,
     const float* __restrict__ w, const uint8_t* __restrict__ cand, int32_t cand_width,
-    int32_t cand_block, int32_t n_tokens, int64_t n_queries, int64_t start_pos,
-    int32_t ratio, int32_t n_heads, int64_t n_rows, float* __restrict__ scores,
-    int64_t scores_ld, int32_t rows_per_wave, int32_t waves_per_query) {
-  constexpr int KS = DI / 32;
+    int32_t cand_block, int32_t n_tokens, int64_t start_pos, int32_t ratio, int32_t n_heads,
+    int32_t n_rows, float* __restrict__ scores, int64_t scores_ld, int32_t blocks_per_query) {
+  using KT = KeyTile<DI>;
+  constexpr int KS = KT::KS;
+  constexpr int kQBytes = 16 * HT * DI * 2;
+  constexpr int kRingBytes = kStages * KT::kBytes;
+  constexpr int kAux = NT ? 2 : 0;  // nt: no reuse expected
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kQBytes + 64 * 4 + kWaves * kRingBytes];
+  uint8_t* const qs = smem;
+  float* const ws = reinterpret_cast<float*>(smem + kQBytes);
+
   const int lane = threadIdx.x & 63;
-  const int64_t wv = (int64_t)blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-  const int64_t q = wv / waves_per_query;
-  if (q >= n_queries) return;
-  const int64_t part = wv - q * waves_per_query;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int64_t q = blockIdx.x / blocks_per_query;
+  const int wpq = blocks_per_query * kWaves;
+  const int part = (int)(blockIdx.x - q * blocks_per_query) * kWaves + wave;
   const int64_t b = q / n_tokens;
   const int64_t t = q - b * n_tokens;
-  int64_t n_vis = (start_pos + t + 1) / ratio;
-  if (n_vis > n_rows) n_vis = n_rows;
-  const int64_t j_begin = part * rows_per_wave;
-  int64_t j_end = j_begin + rows_per_wave;
-  if (j_end > n_rows) j_end = n_rows;
-  if (j_begin >= j_end) return;
-  const int64_t live_end = j_end < n_vis ? j_end : n_vis;
+  int64_t vis = (start_pos + t + 1) / ratio;
+  const int live_end = (int)(vis < n_rows ? vis : n_rows);
+  const int nbt = (n_rows + 15) / 16;     // 16-key blocks in the row
+  const int nbv = (live_end + 15) / 16;   // ... with a visible key
+  const int nw = part < nbv ? (nbv - 1 - part) / wpq + 1 : 0;  // this wavefront's visible blocks
 
   float* __restrict__ srow = scores + q * scores_ld;
   const float kNegInf = -__builtin_huge_valf();
-  for (int64_t j = (j_begin > live_end ? j_begin : live_end) + lane; j < j_end; j += kWave)
-    srow[j] = kNegInf;
-  if (j_begin >= live_end) return;
 
-  const int r16 = lane & 15;
-  const int g = lane >> 4;
+  uint8_t* const ring = smem + kQBytes + 64 * 4 + wave * kRingBytes;
+  const uint16_t* __restrict__ kb = kI + b * kI_bs;
+
+  // ---- first kStages blocks in flight, then the query through LDS
+#pragma unroll
+  for (int s = 0; s < kStages; ++s)
+    if (s < nw) issue_block<DI, kAux>(kb, (part + s * wpq) * 16, live_end, lane, ring + s * KT::kBytes);
+  {
+    const uint16_t* qrow = qI + q * n_heads * DI;
+    for (int e = threadIdx.x; e < 16 * HT * KT::CPR; e += kThreads) {
+      const int h = e / KT::CPR;
+      const int c = e % KT::CPR;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (h < n_heads) v = *reinterpret_cast<const u32x4*>(qrow + h * DI + 8 * c);
+      *reinterpret_cast<u32x4*>(qs + h * 2 * DI + 16 * (c ^ KT::swz(h))) = v;
+    }
+    if (threadIdx.x < 64) ws[threadIdx.x] = (int)threadIdx.x < n_heads ? w[q * n_heads + threadIdx.x] : 0.0f;
+  }
+  lds_barrier();
+
+  // lane offsets of its k-step operands in a block (row r16, chunks g + 4kk)
+  uint32_t off[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk)
+    off[kk] = (uint32_t)(r16 * 2 * DI + 16 * ((g + 4 * kk) ^ KT::swz(r16)));
+  const uint32_t ring_lds = (uint32_t)(size_t)(lds_void*)(size_t)ring;
+  const uint32_t qs_lds = (uint32_t)(size_t)(lds_void*)(size_t)qs;
 
   bf16x8 afr[HT][KS];
   float wh[HT][4];
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
-    const int h = 16 * ht + r16;
-    const uint16_t* qp = qI + (q * n_heads + h) * DI + 8 * g;
+    u32x4 v[KS];
+    lds_read_ks<KS>(v, off, qs_lds + ht * 16 * 2 * DI);
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (h < n_heads) v = *reinterpret_cast<const u32x4*>(qp + 32 * kk);
-      afr[ht][kk] = as_bf16x8(v);
-    }
+    for (int kk = 0; kk < KS; ++kk) afr[ht][kk] = as_bf16x8(v[kk]);
+    u32x4 wv;
+    const uint32_t wa = (uint32_t)(size_t)(lds_void*)(size_t)(ws + 16 * ht + 4 * g);
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(wv) : "v"(wa) : "memory");
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = 16 * ht + 4 * g + i;
-      wh[ht][i] = hh < n_heads ? w[q * n_heads + hh] : 0.0f;
+    for (int i = 0; i < 4; ++i) wh[ht][i] = __uint_as_float(wv[i]);
+  }
+
+  // ---- invisible blocks of this wavefront: -inf
+  for (int blk = part + nw * wpq; blk < nbt; blk += wpq) {
+    const int j = blk * 16 + lane;
+    if (lane < 16 && j < n_rows) srow[j] = kNegInf;
+  }
+
+  // ---- the stream
+  for (int i0 = 0; i0 < nw; i0 += kStages) {
+#pragma unroll
+    for (int s = 0; s < kStages; ++s) {
+      const int i = i0 + s;
+      if (i < nw) {
+        if (i + kStages - 1 < nw) wait_vmcnt<KS * (kStages - 1)>();
+        else wait_vmcnt<0>();
+        u32x4 kf[KS];
+        lds_read_ks<KS>(kf, off, ring_lds + s * KT::kBytes);
+        if (i + kStages < nw)
+          issue_block<DI, kAux>(kb, (part + (i + kStages) * wpq) * 16, live_end, lane,
+                                ring + s * KT::kBytes);
+        f32x4 acc[HT];
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht) acc[ht] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          const bf16x8 bk = as_bf16x8(kf[kk]);
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma16x16x32(afr[ht][kk], bk, acc[ht]);
+        }
+        float sum = 0.0f;
+#pragma unroll
+        for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sum += wh[ht][e] * fmaxf(acc[ht][e], 0.0f);
+        sum += __shfl_xor(sum, 16);
+        sum += __shfl_xor(sum, 32);
+        const int j = (part + i * wpq) * 16 + r16;
+        if (g == 0 && j < n_rows) srow[j] = j < live_end ? sum : kNegInf;
+      }
     }
   }
 
-  const uint16_t* __restrict__ kb = kI + b * kI_bs + 8 * g;
-  const uint8_t* __restrict__ crow = cand ? cand + q * cand_width : nullptr;
-
-  // positions stay below 2^31 (checked by the C ABI), so 32-bit division
-  auto allowed = [&](int64_t j) -> bool {
-    return j < live_end && (crow == nullptr || crow[(uint32_t)j / (uint32_t)cand_block] != 0);
-  };
-  auto load_block = [&](int64_t j0, u32x4 (&buf)[KS]) {
-    const int64_t j = j0 + r16;
-    const bool ok = allowed(j);
-    const uint16_t* p = kb + (ok ? j : j0) * DI;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (ok) v = *reinterpret_cast<const u32x4*>(p + 32 * kk);
-      buf[kk] = v;
+  // ---- candidate mask: the same lanes overwrite their masked scores
+  if (cand != nullptr && g == 0) {
+    const uint8_t* __restrict__ crow = cand + q * cand_width;
+    for (int i = 0; i < nw; ++i) {
+      const int j = (part + i * wpq) * 16 + r16;
+      if (j < live_end && crow[(uint32_t)j / (uint32_t)cand_block] == 0) srow[j] = kNegInf;
     }
-  };
-
-  u32x4 cur[KS], nxt[KS];
-  load_block(j_begin, cur);
-  for (int64_t j0 = j_begin; j0 < live_end; j0 += 16) {
-    const int64_t jn = j0 + 16;
-    if (jn < live_end) load_block(jn, nxt);
-    f32x4 acc[HT];
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht) acc[ht] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const bf16x8 bk = as_bf16x8(cur[kk]);
-#pragma unroll
-      for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma16x16x32(afr[ht][kk], bk, acc[ht]);
-    }
-    float part_sum = 0.0f;
-#pragma unroll
-    for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) part_sum += wh[ht][i] * fmaxf(acc[ht][i], 0.0f);
-    part_sum += __shfl_xor(part_sum, 16);
-    part_sum += __shfl_xor(part_sum, 32);
-    const int64_t j = j0 + r16;
-    if (g == 0 && j < live_end) srow[j] = allowed(j) ? part_sum : kNegInf;
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) cur[kk] = nxt[kk];
   }
 }
 
-template <int DI>
+template <int DI, int NT>
 hipError_t dispatch_heads(int ht, dim3 grid, hipStream_t s, const uint16_t* qI,
                           const uint16_t* kI, int64_t kI_bs, const float* w,
                           const uint8_t* cand, int32_t cand_width, int32_t cand_block,
-                          int32_t n_tokens, int64_t nq, int64_t start_pos, int32_t ratio,
-                          int32_t n_heads, int64_t n_rows, float* scores, int64_t scores_ld,
-                          int32_t rpw, int32_t wpq) {
-#define V41_IDX_LAUNCH(HT_)                                                                  \
-  hipLaunchKernelGGL((indexer_kernel<DI, HT_>), grid, dim3(256), 0, s, qI, kI, kI_bs, w,    \
-                     cand, cand_width, cand_block, n_tokens, nq, start_pos, ratio, n_heads, \
-                     n_rows, scores, scores_ld, rpw, wpq)
+                          int32_t n_tokens, int64_t start_pos, int32_t ratio,
+                          int32_t n_heads, int32_t n_rows, float* scores, int64_t scores_ld,
+                          int32_t bpq) {
+#define V41_IDX_LAUNCH(HT_)                                                                   \
+  hipLaunchKernelGGL((indexer_kernel<DI, HT_, NT>), grid, dim3(kThreads), 0, s, qI, kI,      \
+                     kI_bs, w, cand, cand_width, cand_block, n_tokens, start_pos, ratio,     \
+                     n_heads, n_rows, scores, scores_ld, bpq)
   switch (ht) {
     case 1: V41_IDX_LAUNCH(1); break;
     case 2: V41_IDX_LAUNCH(2); break;
@@ -137,6 +255,21 @@ hipError_t dispatch_heads(int ht, dim3 grid, hipStream_t s, const uint16_t* qI,
   }
 #undef V41_IDX_LAUNCH
   return hipGetLastError();
+}
+
+template <int DI>
+hipError_t dispatch_nt(bool nt, int ht, dim3 grid, hipStream_t s, const uint16_t* qI,
+                       const uint16_t* kI, int64_t kI_bs, const float* w, const uint8_t* cand,
+                       int32_t cand_width, int32_t cand_block, int32_t n_tokens,
+                       int64_t start_pos, int32_t ratio, int32_t n_heads, int32_t n_rows,
+                       float* scores, int64_t scores_ld, int32_t bpq) {
+  if (nt)
+    return dispatch_heads<DI, 1>(ht, grid, s, qI, kI, kI_bs, w, cand, cand_width, cand_block,
+                                 n_tokens, start_pos, ratio, n_heads, n_rows, scores,
+                                 scores_ld, bpq);
+  return dispatch_heads<DI, 0>(ht, grid, s, qI, kI, kI_bs, w, cand, cand_width, cand_block,
+                               n_tokens, start_pos, ratio, n_heads, n_rows, scores, scores_ld,
+                               bpq);
 }
 
 }  // namespace
@@ -149,30 +282,33 @@ hipError_t launch_indexer_scores(const uint16_t* qI, const uint16_t* kI, int64_t
                                  int64_t scores_ld, hipStream_t s) {
   const int64_t nq = (int64_t)batch * n_tokens;
   if (nq == 0 || n_rows == 0) return hipSuccess;
-  // Rows per wavefront: enough wavefronts to keep HBM busy (~2k), at most 256
-  // keys (64 KB at DI = 128) per wavefront so its qI fragments stay amortised.
-  int64_t rpw = (nq * n_rows + 2047) / 2048;
-  rpw = (rpw + 15) / 16 * 16;
-  if (rpw < 32) rpw = 32;
-  if (rpw > 256) rpw = 256;
-  const int64_t wpq = (n_rows + rpw - 1) / rpw;
-  const int64_t waves = nq * wpq;
-  const int64_t blocks = (waves + kWavesPerBlock - 1) / kWavesPerBlock;
+  // Workgroups per query: about 384 over the whole grid (1.5 per CU; up to 3
+  // fit in LDS), the best measured for decode at 16 and 64 sequences, but at
+  // least two 16-key blocks for each wavefront.
+  const int64_t nbt = (n_rows + 15) / 16;
+  int64_t bpq = (384 + nq / 2) / nq;
+  const int64_t bpq_max = nbt / (2 * kWaves);
+  if (bpq > bpq_max) bpq = bpq_max;
+  if (bpq < 1) bpq = 1;
+  if (nq * bpq > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)(nq * bpq));
   const int ht = (n_heads + 15) / 16;
-  const dim3 grid((unsigned)blocks);
+  // a key serves one query at a decode step: stream it past the caches
+  const bool nt = n_tokens == 1;
+  const int32_t rows = (int32_t)n_rows;
   switch (head_dim) {
     case 32:
-      return dispatch_heads<32>(ht, grid, s, qI, kI, kI_bs, w, cand, cand_width, cand_block,
-                                n_tokens, nq, start_pos, ratio, n_heads, n_rows, scores,
-                                scores_ld, (int32_t)rpw, (int32_t)wpq);
+      return dispatch_nt<32>(nt, ht, grid, s, qI, kI, kI_bs, w, cand, cand_width, cand_block,
+                             n_tokens, start_pos, ratio, n_heads, rows, scores, scores_ld,
+                             (int32_t)bpq);
     case 64:
-      return dispatch_heads<64>(ht, grid, s, qI, kI, kI_bs, w, cand, cand_width, cand_block,
-                                n_tokens, nq, start_pos, ratio, n_heads, n_rows, scores,
-                                scores_ld, (int32_t)rpw, (int32_t)wpq);
+      return dispatch_nt<64>(nt, ht, grid, s, qI, kI, kI_bs, w, cand, cand_width, cand_block,
+                             n_tokens, start_pos, ratio, n_heads, rows, scores, scores_ld,
+                             (int32_t)bpq);
     default:
-      return dispatch_heads<128>(ht, grid, s, qI, kI, kI_bs, w, cand, cand_width, cand_block,
-                                 n_tokens, nq, start_pos, ratio, n_heads, n_rows, scores,
-                                 scores_ld, (int32_t)rpw, (int32_t)wpq);
+      return dispatch_nt<128>(nt, ht, grid, s, qI, kI, kI_bs, w, cand, cand_width, cand_block,
+                              n_tokens, start_pos, ratio, n_heads, rows, scores, scores_ld,
+                              (int32_t)bpq);
   }
 }
 
