@@ -3,9 +3,13 @@
 // S = Q G / sqrt(d), A = exp S / (exp s_h + sum exp S), O = sum A G; the
 // sparse_attn contract of the "deepseek_v41_ref::attn" rustdoc), for gfx950.
 //
-// One latent row is key and value for every head, so a workgroup takes a
-// query and 64 of its heads (16 per wavefront) and streams the query's valid
-// rows through LDS in tiles of 32:
+// Two forms share the row handling below.  The wide form (many queries, e.g.
+// a prefill chunk) is described here; the narrow form (few queries, decode)
+// follows its own comment further down.
+//
+// One latent row is key and value for every head, so a wide workgroup takes
+// a query and 64 of its heads (16 per wavefront) and streams the query's
+// valid rows through LDS in tiles of 32:
 //  * the idx row is compacted first (entries outside the two row sources are
 //    dropped), so -1 padding costs neither loads nor matrix-core time;
 //  * gather: rows go from HBM straight into LDS with global_load_lds_dwordx4
@@ -23,9 +27,9 @@
 //    B operand is the probabilities exactly as the S^T accumulator left them
 //    in the lane (the transposing loads fetch the rows in that order), rounded
 //    to bf16.
-// Decode has few queries: a query's rows are then split over several
-// workgroups, each writing an f32 partial (max, sum, O), and a combine kernel
-// merges them.
+// When even the narrow grid does not cover the compute units, a query's rows
+// are split over several workgroups, each writing an f32 partial (max, sum,
+// O), and a combine kernel merges them.
 #include "v41_common.h"
 
 namespace v41 {
@@ -58,20 +62,26 @@ struct Params {
   int32_t splits;
 };
 
-// LDS placement of a 32-row tile.  A wavefront load instruction fills one
-// 1 KB block (RPI rows of D values); blocks are padded by 32 bytes.  For
-// D = 512 the 16-byte chunk c of row r sits at chunk c ^ ((r >> 3) & 1).
-template <int D>
+// LDS placement of a tile of ROWS rows.  A wavefront load instruction fills
+// one 1 KB block (RPI rows of D values); blocks are padded by 32 bytes, so
+// rows r .. r+3 start 32 bytes apart mod 128.  For D = 512 the 16-byte chunk
+// c of row r sits at chunk c ^ (bit 2 of r ^ bit 3 of r): the 8 (16) lanes
+// an LDS cycle serves when 16 consecutive rows touch one chunk index then
+// hit 8 (16) distinct 16-byte bank groups, and the transposing reads (4 rows
+// of 32 bytes per 16 lanes, rows 4k .. 4k+3) share one permutation.
+template <int D, int ROWS>
 struct Tile {
   static constexpr int LPR = D / 8;      // 16-byte chunks per row
   static constexpr int RPI = 64 / LPR;   // rows per load instruction
   static constexpr int kBlkBytes = 1024 + 32;
-  static constexpr int kBlocks = kTile / RPI;
+  static constexpr int kBlocks = ROWS / RPI;
   static constexpr int kBufBytes = kBlocks * kBlkBytes;
   static __device__ __forceinline__ int row_off(int r) {
     return (r / RPI) * kBlkBytes + (r % RPI) * (2 * D);
   }
-  static __device__ __forceinline__ int swz(int r) { return D == 512 ? ((r >> 3) & 1) : 0; }
+  static __device__ __forceinline__ int swz(int r) {
+    return D == 512 ? (((r >> 2) ^ (r >> 3)) & 1) : 0;
+  }
 };
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -98,13 +108,77 @@ __device__ __forceinline__ void tr_load4(u32x2 (&t)[8], uint32_t lo, uint32_t hi
       : "memory");
 }
 
+// The same for N = 1, 2 or 4 M-tiles.
+template <int N>
+__device__ __forceinline__ void tr_load(u32x2 (&t)[2 * N], uint32_t lo, uint32_t hi) {
+  if constexpr (N == 4) {
+    tr_load4(t, lo, hi);
+  } else if constexpr (N == 2) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4\n\t"
+        "ds_read_b64_tr_b16 %1, %5\n\t"
+        "ds_read_b64_tr_b16 %2, %4 offset:32\n\t"
+        "ds_read_b64_tr_b16 %3, %5 offset:32\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3])
+        : "v"(lo), "v"(hi)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %2\n\t"
+        "ds_read_b64_tr_b16 %1, %3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(t[0]), "=&v"(t[1])
+        : "v"(lo), "v"(hi)
+        : "memory");
+  }
+}
+
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Compacts the usable entries of an idx row (0 <= ix < total_rows, in their
+// order) into list and returns how many there are.  Every thread of the
+// workgroup (kW wavefronts) calls it; each wavefront scans a contiguous share
+// of the row.
+template <int kW>
+__device__ __forceinline__ uint32_t compact_idx(const int32_t* __restrict__ irow, int width,
+                                                int64_t total_rows, int32_t* list,
+                                                uint32_t* wave_cnt, int wave, int lane) {
+  const int per_wave = ((width + kW * kWave - 1) / (kW * kWave)) * kWave;
+  const int w0 = wave * per_wave;
+  int w1 = w0 + per_wave;
+  if (w1 > width) w1 = width;
+  uint32_t cnt = 0;
+  for (int i0 = w0; i0 < w1; i0 += kWave) {
+    const int i = i0 + lane;
+    const int32_t ix = (i < w1) ? irow[i] : -1;
+    const bool ok = ix >= 0 && (int64_t)ix < total_rows;
+    cnt += __popcll(__ballot(ok));
+  }
+  if (lane == 0) wave_cnt[wave] = cnt;
+  __syncthreads();
+  uint32_t base = 0;
+  for (int w = 0; w < wave; ++w) base += wave_cnt[w];
+  for (int i0 = w0; i0 < w1; i0 += kWave) {
+    const int i = i0 + lane;
+    const int32_t ix = (i < w1) ? irow[i] : -1;
+    const bool ok = ix >= 0 && (int64_t)ix < total_rows;
+    const unsigned long long bal = __ballot(ok);
+    const uint32_t before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (ok) list[base + before] = ix;
+    base += __popcll(bal);
+  }
+  __syncthreads();
+  uint32_t n_valid = 0;
+  for (int w = 0; w < kW; ++w) n_valid += wave_cnt[w];
+  return n_valid;
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_kernel(Params p) {
-  using TL = Tile<D>;
+  using TL = Tile<D, kTile>;
   constexpr int KS = D / 32;  // QK K-steps
   constexpr int MT = D / 16;  // PV M-tiles (dims)
   __shared__ __attribute__((aligned(16))) uint8_t tiles[2 * TL::kBufBytes];
@@ -123,37 +197,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(Params p) {
   const bool head_ok = head < p.n_heads;
   const int64_t total_rows = p.rows_a_len + p.rows_b_len;
 
-  // ---- compact the idx row: each wave takes a contiguous quarter
-  const int32_t* irow = p.idx + qi * p.idx_ld;
-  {
-    const int per_wave = ((p.width + 4 * kWave - 1) / (4 * kWave)) * kWave;
-    const int w0 = wave * per_wave;
-    int w1 = w0 + per_wave;
-    if (w1 > p.width) w1 = p.width;
-    uint32_t cnt = 0;
-    for (int i0 = w0; i0 < w1; i0 += kWave) {
-      const int i = i0 + lane;
-      const int32_t ix = (i < w1) ? irow[i] : -1;
-      const bool ok = ix >= 0 && (int64_t)ix < total_rows;
-      cnt += __popcll(__ballot(ok));
-    }
-    if (lane == 0) wave_cnt[wave] = cnt;
-    __syncthreads();
-    uint32_t base = 0;
-    for (int w = 0; w < wave; ++w) base += wave_cnt[w];
-    for (int i0 = w0; i0 < w1; i0 += kWave) {
-      const int i = i0 + lane;
-      const int32_t ix = (i < w1) ? irow[i] : -1;
-      const bool ok = ix >= 0 && (int64_t)ix < total_rows;
-      const unsigned long long bal = __ballot(ok);
-      const uint32_t before = __popcll(bal & ((1ull << lane) - 1ull));
-      if (ok) list[base + before] = ix;
-      base += __popcll(bal);
-    }
-  }
-  __syncthreads();
-  uint32_t n_valid = 0;
-  for (int w = 0; w < kThreads / kWave; ++w) n_valid += wave_cnt[w];
+  const uint32_t n_valid = compact_idx<kThreads / kWave>(p.idx + qi * p.idx_ld, p.width,
+                                                         total_rows, list, wave_cnt, wave, lane);
   const int n_tiles = (int)((n_valid + kTile - 1) / kTile);
   const int tps = (n_tiles + p.splits - 1) / p.splits;
   const int t_begin = split * tps;
@@ -315,6 +360,305 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(Params p) {
   }
 }
 
+// ---------------------------------------------------------------- narrow form
+// Few queries (decode): a workgroup takes one query, 16 heads and the query's
+// rows (or one split of them), so a query spreads over several compute units
+// without partial results.  The workgroups of one row set sit 8 apart in the
+// grid (one XCD under round-robin dispatch) and share its rows in that L2.
+// Eight wavefronts (two per SIMD, so one hides the other's latencies) each
+// work alone on every eighth 16-row tile with their own online softmax, and
+// are merged at the end:
+//  * the 16 heads' queries sit in LDS and feed the QK B operand;
+//  * a lane loads its 16 x 16 bytes of a tile straight into the layout of the
+//    QK A operand, one tile ahead;
+//  * QK: 16 rows x 16 heads over four independent accumulators; the S
+//    accumulator is laid out as the B operand of a 16x16x16 PV product, so
+//    the bf16 probabilities never leave the lane;
+//  * the rows go to the wavefront's own LDS slot and come back transposed
+//    (ds_read_b64_tr_b16) as the A operand of O^T += G^T P^T, all D dims;
+//  * head maxima and sums across the lane groups use permlane swaps;
+//  * no barrier inside the loop; at the end the eight (max, sum, O) are
+//    merged through LDS, half of the dims at a time.
+constexpr int kWaveRows = 16;
+constexpr int kNarrowHeads = 16;
+constexpr int kNarrowThreads = 512;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma16x16x16(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// v combined (max or sum) over the four 16-lane groups of the wavefront.
+__device__ __forceinline__ float group_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float group_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
+// Eight ds_read_b64_tr_b16 at 32-byte steps (eight 16-dim M-tiles of one
+// 16-row K block) and a wait for them.
+__device__ __forceinline__ void tr_load8(u32x2 (&t)[8], uint32_t a) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %8 offset:32\n\t"
+      "ds_read_b64_tr_b16 %2, %8 offset:64\n\t"
+      "ds_read_b64_tr_b16 %3, %8 offset:96\n\t"
+      "ds_read_b64_tr_b16 %4, %8 offset:128\n\t"
+      "ds_read_b64_tr_b16 %5, %8 offset:160\n\t"
+      "ds_read_b64_tr_b16 %6, %8 offset:192\n\t"
+      "ds_read_b64_tr_b16 %7, %8 offset:224\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]),
+        "=&v"(t[6]), "=&v"(t[7])
+      : "v"(a)
+      : "memory");
+}
+
+__device__ __forceinline__ void tr_load4_1(u32x2 (&t)[4], uint32_t a) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n\t"
+      "ds_read_b64_tr_b16 %1, %4 offset:32\n\t"
+      "ds_read_b64_tr_b16 %2, %4 offset:64\n\t"
+      "ds_read_b64_tr_b16 %3, %4 offset:96\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3])
+      : "v"(a)
+      : "memory");
+}
+
+// A wavefront's 16-row LDS slot: rows 2D + 32 bytes apart (rows r .. r+3 at
+// distinct 32-byte bank groups mod 128); 16-byte chunk c of row r at chunk
+// c ^ (bit 2 of r ^ bit 3 of r), so the row stores (8 or 16 rows, one chunk
+// index per LDS cycle) and the transposing reads (rows 4k .. 4k+3, 32 bytes
+// each, per 16 lanes) are both free of bank conflicts.
+template <int D>
+struct WaveSlot {
+  static constexpr int kStride = 2 * D + 32;
+  static constexpr int kBytes = kWaveRows * kStride;
+  static __device__ __forceinline__ int swz(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
+};
+
+template <int D>
+__global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p,
+                                                                        int32_t head_groups,
+                                                                        int64_t n_units) {
+  using WS = WaveSlot<D>;
+  constexpr int kW = kNarrowThreads / kWave;
+  constexpr int KS = D / 32;     // QK K-steps (16-byte chunks per lane and row)
+  constexpr int DT = D / 16;     // PV M-tiles (all dims)
+  constexpr int kHalfDT = DT / 2;
+  constexpr int kQStride = 2 * D + 16;  // bytes per head row of the query tile
+  static_assert(kW * kHalfDT * kWave * 16 <= kW * WS::kBytes, "merge area");
+  __shared__ __attribute__((aligned(16))) uint8_t slots[kW * WS::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t qs[kNarrowHeads * kQStride];
+  __shared__ int32_t list[kMaxWidth];
+  __shared__ uint32_t wave_cnt[kW];
+  __shared__ float xm[kW][kNarrowHeads];
+  __shared__ float xl[kW][kNarrowHeads];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int grp = blockIdx.x >> 3;
+  const int hg = grp % head_groups;
+  const int64_t unit = (int64_t)(grp / head_groups) * 8 + (blockIdx.x & 7);
+  if (unit >= n_units) return;  // whole workgroup
+  const int64_t qi = unit / p.splits;
+  const int split = (int)(unit - qi * p.splits);
+  const int64_t b = qi / p.n_tokens;
+  const int head = hg * kNarrowHeads + r16;
+  const bool head_ok = head < p.n_heads;
+  const int64_t total_rows = p.rows_a_len + p.rows_b_len;
+
+  // ---- the 16 heads' queries into LDS (zero rows past n_heads); the
+  // compaction's barriers publish them
+  {
+    constexpr int CPR = D / 8;
+    const uint16_t* q0 = p.q + (qi * p.n_heads + hg * kNarrowHeads) * D;
+    for (int e = tid; e < kNarrowHeads * CPR; e += kNarrowThreads) {
+      const int h = e / CPR, c = e % CPR;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (hg * kNarrowHeads + h < p.n_heads) v = *reinterpret_cast<const u32x4*>(q0 + h * D + 8 * c);
+      *reinterpret_cast<u32x4*>(qs + h * kQStride + 16 * c) = v;
+    }
+  }
+  const uint32_t n_valid = compact_idx<kW>(p.idx + qi * p.idx_ld, p.width, total_rows, list,
+                                           wave_cnt, wave, lane);
+  const int n_tiles = (int)((n_valid + kWaveRows - 1) / kWaveRows);
+  const int tps = (n_tiles + p.splits - 1) / p.splits;
+  const int t_begin = split * tps;
+  const int t_end = (t_begin + tps < n_tiles) ? t_begin + tps : n_tiles;
+  // this wavefront's tiles: t_begin + wave + kW i
+  const int nw = (t_begin + wave < t_end) ? (t_end - t_begin - wave + kW - 1) / kW : 0;
+
+  // ---- a lane's share of a tile: row r16, chunks 4kk + g (rows past n_valid
+  // repeat the first valid row: finite data, probability 0)
+  const uint16_t* a_base = p.rows_a + b * p.a_bs;
+  const uint16_t* b_base = p.rows_b + b * p.b_bs;
+  auto load = [&](int i, u32x4 (&rb)[KS]) {
+    int pos = (t_begin + wave + kW * i) * kWaveRows + r16;
+    if ((uint32_t)pos >= n_valid) pos = 0;
+    const int64_t ix = list[pos];
+    const uint16_t* src =
+        ((ix < p.rows_a_len) ? a_base + ix * D : b_base + (ix - p.rows_a_len) * D) + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) rb[kk] = *reinterpret_cast<const u32x4*>(src + 32 * kk);
+  };
+
+  const float sink2 = head_ok ? p.sink[head] * kLog2e : 0.0f;
+  const float kNegInf = -__builtin_huge_valf();
+  float m2 = sink2;  // this wavefront's reference max on the log2 scale
+  float l_part = 0.0f;
+  f32x4 acc_o[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc_o[dt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  uint8_t* const slot = slots + wave * WS::kBytes;
+  const int st_off = r16 * WS::kStride + 16 * (g ^ WS::swz(r16));  // + 64 kk
+  const uint8_t* const q_frag = qs + r16 * kQStride + 16 * g;      // + 64 kk
+  //  transposing loads: lane (g, j, q) reads 8 bytes of row 4g + j at dims 4q..
+  const int tj = (lane >> 2) & 3, tq = lane & 3;
+  const int tr_row = 4 * g + tj;
+  const uint32_t tr_addr = (uint32_t)(size_t)(lds_void*)(size_t)(
+      slot + tr_row * WS::kStride + 16 * ((tq >> 1) ^ WS::swz(tr_row)) + 8 * (tq & 1));
+
+  u32x4 rb[KS];
+  if (nw > 0) load(0, rb);
+  for (int i = 0; i < nw; ++i) {
+    // S^T: rows 4g + e of the tile, head r16
+    f32x4 sa[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sa[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const u32x4 qv = *reinterpret_cast<const u32x4*>(q_frag + 64 * kk);
+      sa[kk & 3] = mfma16x16x32(as_bf16x8(rb[kk]), as_bf16x8(qv), sa[kk & 3]);
+    }
+    const f32x4 sacc = (sa[0] + sa[1]) + (sa[2] + sa[3]);
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) *reinterpret_cast<u32x4*>(slot + st_off + 64 * kk) = rb[kk];
+    if (i + 1 < nw) load(i + 1, rb);
+
+    const int rbase = (t_begin + wave + kW * i) * kWaveRows + 4 * g;
+    float sv[4];
+    float mx = kNegInf;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float v = sacc[e] * p.scale_log2;
+      if ((uint32_t)(rbase + e) >= n_valid) v = kNegInf;
+      sv[e] = v;
+      mx = fmaxf(mx, v);
+    }
+    mx = group_max(mx);
+    if (__any(mx > m2 + kRescaleLog2)) {
+      const float m_new = fmaxf(m2, mx);
+      const float alpha = (m_new == m2) ? 1.0f : exp2f(m2 - m_new);
+      m2 = m_new;
+      l_part *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc_o[dt] *= alpha;
+    }
+    u32x2 pk;
+#pragma unroll
+    for (int e = 0; e < 4; e += 2) {
+      const float p0 = (sv[e] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(sv[e] - m2);
+      const float p1 = (sv[e + 1] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(sv[e + 1] - m2);
+      l_part += p0 + p1;
+      const __bf16 b0 = (__bf16)p0, b1 = (__bf16)p1;
+      pk[e / 2] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+    }
+    // O^T[dims][head] += G^T[dims][16 rows] P^T[16 rows][head]
+    if constexpr (DT >= 8) {
+#pragma unroll
+      for (int d0 = 0; d0 < DT; d0 += 8) {
+        u32x2 t[8];
+        tr_load8(t, tr_addr + 32 * d0);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc_o[d0 + j] = mfma16x16x16(t[j], pk, acc_o[d0 + j]);
+      }
+    } else {
+      u32x2 t[4];
+      tr_load4_1(t, tr_addr);
+#pragma unroll
+      for (int j = 0; j < DT; ++j) acc_o[j] = mfma16x16x16(t[j], pk, acc_o[j]);
+    }
+  }
+
+  // ---- merge the wavefronts: M = max m_w, O = sum 2^(m_w - M) O_w,
+  // l = sum 2^(m_w - M) l_w
+  const float l_w = group_sum(l_part);
+  if (g == 0) {
+    xm[wave][r16] = m2;
+    xl[wave][r16] = l_w;
+  }
+  lds_barrier();
+  float M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) M = fmaxf(M, xm[w][r16]);
+  float l_tot = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) {
+    const float mw = xm[w][r16];
+    l_tot += (mw == kNegInf) ? 0.0f : xl[w][r16] * exp2f(mw - M);
+  }
+  const float my_w = (m2 == kNegInf) ? 0.0f : exp2f(m2 - M);
+  const float sink_term = (sink2 == kNegInf) ? 0.0f : exp2f(sink2 - M);
+  const float den = l_tot + sink_term;
+  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+  f32x4* const merge = reinterpret_cast<f32x4*>(slots);  // [wave][half dim-tile][lane]
+  constexpr int kPerWave = kHalfDT / kW;  // dim-tiles each wavefront finishes per half
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int j = 0; j < kHalfDT; ++j)
+      merge[(wave * kHalfDT + j) * kWave + lane] = acc_o[h * kHalfDT + j] * my_w;
+    lds_barrier();
+    if (kPerWave > 0 || wave < kHalfDT) {
+      const int j0 = kPerWave > 0 ? wave * kPerWave : wave;
+      const int jn = kPerWave > 0 ? kPerWave : 1;
+      for (int jj = 0; jj < jn; ++jj) {
+        const int j = j0 + jj;
+        f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < kW; ++w) o += merge[(w * kHalfDT + j) * kWave + lane];
+        const int dim = 16 * (h * kHalfDT + j) + 4 * g;  // lane: dims dim .. dim+3, head r16
+        if (!head_ok) continue;
+        if (p.splits == 1) {
+          uint2 v;
+          v.x = f32_to_bf16_bits(o[0] * inv) | (f32_to_bf16_bits(o[1] * inv) << 16);
+          v.y = f32_to_bf16_bits(o[2] * inv) | (f32_to_bf16_bits(o[3] * inv) << 16);
+          *reinterpret_cast<uint2*>(p.out + (qi * p.n_heads + head) * D + dim) = v;
+        } else {
+          const int64_t slot_i = (qi * p.splits + split) * p.n_heads + head;
+          *reinterpret_cast<f32x4*>(p.part_o + slot_i * D + dim) = o;
+        }
+      }
+    }
+    lds_barrier();
+  }
+  if (p.splits > 1 && head_ok && wave == 0 && g == 0) {
+    const int64_t slot_i = (qi * p.splits + split) * p.n_heads + head;
+    p.part_ml[2 * slot_i] = M;
+    p.part_ml[2 * slot_i + 1] = l_tot;
+  }
+}
+
 // Merge the row splits of each (query, head): M = max_s m_s,
 // den = sum_s l_s 2^(m_s - M) + 2^(sink - M), o = sum_s O_s 2^(m_s - M) / den.
 template <int D>
@@ -351,6 +695,12 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   *reinterpret_cast<uint2*>(out + (qi * n_heads + h) * D + 4 * d4) = o;
 }
 
+// The narrow form serves shapes whose wide grid (one workgroup per query and
+// 64 heads) would not cover the compute units.
+bool attn_narrow(int64_t queries, int32_t n_heads) {
+  return queries * ((n_heads + kHeadsPerBlock - 1) / kHeadsPerBlock) < 256;
+}
+
 template <int D>
 hipError_t launch_d(const AttnArgs& a, int splits, hipStream_t s) {
   const int64_t nq = (int64_t)a.batch * a.n_tokens;
@@ -377,9 +727,18 @@ hipError_t launch_d(const AttnArgs& a, int splits, hipStream_t s) {
     p.part_o = reinterpret_cast<float*>(a.workspace);
     p.part_ml = p.part_o + nq * splits * a.n_heads * (int64_t)D;
   }
-  const dim3 grid((unsigned)(nq * splits), (unsigned)((a.n_heads + kHeadsPerBlock - 1) /
-                                                      kHeadsPerBlock));
-  hipLaunchKernelGGL((attn_kernel<D>), grid, dim3(kThreads), 0, s, p);
+  if (attn_narrow(nq, a.n_heads)) {
+    const int32_t hg = (a.n_heads + kNarrowHeads - 1) / kNarrowHeads;
+    const int64_t units = nq * splits;
+    const int64_t blocks = 8 * hg * ((units + 7) / 8);
+    if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((attn_narrow_kernel<D>), dim3((unsigned)blocks), dim3(kNarrowThreads), 0,
+                       s, p, hg, units);
+  } else {
+    const dim3 grid((unsigned)(nq * splits), (unsigned)((a.n_heads + kHeadsPerBlock - 1) /
+                                                        kHeadsPerBlock));
+    hipLaunchKernelGGL((attn_kernel<D>), grid, dim3(kThreads), 0, s, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   const int per_q = a.n_heads * (D / 4);
@@ -393,12 +752,14 @@ hipError_t launch_d(const AttnArgs& a, int splits, hipStream_t s) {
 
 int attn_preferred_splits(int32_t queries, int32_t n_heads, int32_t width) {
   // Aim for ~256 workgroups (one per compute unit) when there are few queries,
-  // keeping at least 4 tiles of rows per split.
-  const int64_t hg = (n_heads + kHeadsPerBlock - 1) / kHeadsPerBlock;
+  // keeping at least 2 narrow tiles (4 wide ones) of rows per split.
+  const bool narrow = attn_narrow(queries, n_heads);
+  const int64_t per_wg = narrow ? kNarrowHeads : kHeadsPerBlock;
+  const int64_t hg = (n_heads + per_wg - 1) / per_wg;
   const int64_t wgs = (int64_t)queries * hg;
   if (wgs >= 256) return 1;
   int64_t s = (256 + wgs - 1) / wgs;
-  const int64_t max_s = width / (4 * kTile);
+  const int64_t max_s = narrow ? width / (8 * kWaveRows) : width / (4 * kTile);
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
   if (s > 64) s = 64;

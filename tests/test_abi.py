@@ -97,7 +97,11 @@ def test_attn_rejects_wide_selection_and_missing_rows(lib):
 
 
 def test_workspace_query(lib):
-    # few queries: the call would split rows and asks for scratch
-    assert lib.v41_sparse_attn_workspace_bytes(64, 1, 64, 512, 640) > 0
+    # few queries: the call would split rows and asks for scratch; the size
+    # holds an f32 partial O and (max, sum) per (query, split, head)
+    ws = lib.v41_sparse_attn_workspace_bytes(16, 1, 64, 512, 640)
+    assert ws > 0 and ws % (16 * 64 * (512 * 4 + 8)) == 0
+    # 64 queries x 4 groups of 16 heads already cover the compute units
+    assert lib.v41_sparse_attn_workspace_bytes(64, 1, 64, 512, 640) == 0
     # many queries: no split
     assert lib.v41_sparse_attn_workspace_bytes(1, 2048, 64, 512, 640) == 0
