@@ -312,7 +312,41 @@ def run_workload(name, steps, warmup, n_sets, torch, device):
     return wl, ms_step, kern_us, work
 
 
-def roofline_entry(kname, work, us, bound):
+# Sources of each kernel: a stored traffic figure holds only while they are
+# unchanged.
+KERNEL_SOURCES = {
+    "indexer_scores": ("v41_indexer.hip", "v41_common.h"),
+    "sparse_attn_sink": ("v41_attn.hip", "v41_common.h"),
+    "topk_select": ("v41_topk.hip", "v41_common.h"),
+}
+
+
+def source_digest(kname):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kname, ()):
+        with open(os.path.join(ROOT, "indexer_top_sink_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kname, workload):
+    """HBM bytes per launch from profiles/hbm_traffic.json (FETCH_SIZE + WRITE_SIZE
+    counter runs scaled by a plain copy of known size), or None when absent or
+    taken on other sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        recs = json.load(f)
+    for r in recs:
+        if r["kernel"] == kname and r["workload"] == workload and \
+                r["source_sha256"] == source_digest(kname):
+            return r["bytes_per_launch"]
+    return None
+
+
+def roofline_entry(kname, work, us, bound, workload=None):
     w = work[kname]
     if bound == "hbm":
         achieved = w["bytes"] / (us * 1e-6) / 1e9
@@ -320,8 +354,9 @@ def roofline_entry(kname, work, us, bound):
     else:
         achieved = w["flops"] / (us * 1e-6) / 1e12
         peak, unit = BF16_PEAK_TFLOPS, "TFLOP/s"
+    traffic = measured_traffic(kname, workload) if workload else None
     return {"kernel": kname, "bound": bound, "achieved": round(achieved, 1), "peak": peak,
-            "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
+            "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
             "avg_us": round(us, 2), "algorithmic_bytes": w["bytes"],
             "algorithmic_flops": w["flops"]}
 
@@ -336,6 +371,9 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
+                    help="first copy MB megabytes device to device three times (the "
+                         "known-size kernel that scales HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); each GPU would "
@@ -348,16 +386,27 @@ def main():
     torch.cuda.set_device(device)
     from indexer_top_sink_amd import v41
     v41.load()
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=device)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {n} bytes read and {n} written per copy")
+        del src, dst
 
     wl, ms_step, kern_us, work = run_workload(args.workload, args.steps, args.warmup,
                                               args.input_sets, torch, device)
     tokens = wl.queries
     value = tokens / (ms_step * 1e-3)
-    dominant = max(work, key=lambda k: work[k]["bytes"])
-    if wl.mode == "prefill":
-        dominant = "sparse_attn_sink"
+    # the dominant kernel is the one that takes the most time; decode moves
+    # bytes (HBM bound), a prefill chunk multiplies (MFMA bound)
+    dominant = max(kern_us, key=lambda k: kern_us[k])
     bound = "mfma" if wl.mode == "prefill" else "hbm"
-    roof = roofline_entry(dominant, work, kern_us[dominant], bound)
+    roof = roofline_entry(dominant, work, kern_us[dominant], bound, wl.name)
+    others = {k: roofline_entry(k, work, kern_us[k], bound, wl.name)
+              for k in ("indexer_scores", "sparse_attn_sink") if k != dominant}
 
     step_bytes = sum(v["bytes"] for v in work.values())
     out = {
@@ -373,6 +422,7 @@ def main():
                    "topk": wl.topk, "ratio": wl.ratio, "hip_graph": True,
                    "input_sets": args.input_sets},
         "roofline": roof,
+        "roofline_other": others,
         "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "kernels_us": {k: round(v, 2) for k, v in kern_us.items()},
     }
@@ -384,12 +434,12 @@ def main():
                 "value": round(pw.n_tokens / (pms * 1e-3), 1), "unit": "tokens/s",
                 "ms_per_step": round(pms, 5),
                 "roofline": roofline_entry("sparse_attn_sink", pwork, pk["sparse_attn_sink"],
-                                           "mfma"),
+                                           "mfma", pw.name),
                 "indexer_roofline": roofline_entry("indexer_scores", pwork,
-                                                   pk["indexer_scores"], "mfma"),
+                                                   pk["indexer_scores"], "mfma", pw.name),
                 "kernels_us": {k: round(v, 2) for k, v in pk.items()}}}
     if not args.no_cpu_baseline:
-        n = args.cpu_sample or (8 if wl.mode == "decode" else 32)
+        n = args.cpu_sample or (wl.batch if wl.mode == "decode" else 32)
         t0 = time.time()
         out["cpu_baseline"] = cpu_baseline(wl, n)
         log(f"cpu baseline in {time.time() - t0:.1f}s")
