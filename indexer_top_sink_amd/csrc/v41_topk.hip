@@ -12,7 +12,10 @@
 //  2. radix select of the k-th largest key T: digits of 8 bits of
 //     (key - min), starting at the top bit of (max - min), so the first pass
 //     already spreads over the bins; the LDS histogram is replicated 8 ways
-//     across lanes so that equal digits do not serialise on one word;
+//     across lanes so that equal digits do not serialise on one word; two
+//     histograms alternate so clearing the next one overlaps the counting,
+//     and the first wavefront sums the copies while it scans (two barriers
+//     per pass);
 //  3. the selection is {key > T} plus the first `need` positions with key == T
 //     (ties to the lower position); one block-wide exclusive scan of packed
 //     (greater, equal) counts gives each thread its output slots, and the
@@ -33,7 +36,7 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 
 template <int NT>
 struct TopkShared {
-  uint32_t hist[kHistCopies * 256];
+  uint32_t hist[2][kHistCopies * 256];  // alternate passes; the idle one is cleared
   uint32_t red[3][NT / kWave];
   uint32_t digit, above;
 };
@@ -102,10 +105,13 @@ __device__ __forceinline__ void radix_select(ForKeys for_keys, uint32_t m, uint3
   const int top = 31 - __clz(range);
   int shift = top > 7 ? top - 7 : 0;
   uint32_t prefix = 0u, pmask = 0u, need_r = m;
-  uint32_t* myhist = sh.hist + (lane % kHistCopies) * 256;
-  while (true) {
-    for (int i = tid; i < kHistCopies * 256; i += NT) sh.hist[i] = 0u;
-    __syncthreads();
+  for (int i = tid; i < kHistCopies * 256; i += NT) sh.hist[0][i] = 0u;
+  __syncthreads();
+  for (int pass = 0;; ++pass) {
+    uint32_t* const hist = sh.hist[pass & 1];
+    // the other copy was last read before the previous pass's final barrier
+    for (int i = tid; i < kHistCopies * 256; i += NT) sh.hist[(pass + 1) & 1][i] = 0u;
+    uint32_t* const myhist = hist + (lane % kHistCopies) * 256;
     for_keys([&](uint32_t key) {
       if (key != 0u) {
         const uint32_t d = key - kmin;
@@ -113,19 +119,15 @@ __device__ __forceinline__ void radix_select(ForKeys for_keys, uint32_t m, uint3
       }
     });
     __syncthreads();
-    for (int b = tid; b < 256; b += NT) {
-      uint32_t s = 0;
-#pragma unroll
-      for (int c = 0; c < kHistCopies; ++c) s += sh.hist[c * 256 + b];
-      sh.hist[b] = s;  // only thread b touches column b
-    }
-    __syncthreads();
     if (tid < kWave) {
-      // lane l owns bins 255-4l .. 252-4l; find the bin holding the need_r-th
-      // largest digit, scanning from the top
-      const uint32_t c0 = sh.hist[255 - 4 * lane], c1 = sh.hist[254 - 4 * lane];
-      const uint32_t c2 = sh.hist[253 - 4 * lane], c3 = sh.hist[252 - 4 * lane];
-      const uint32_t s = c0 + c1 + c2 + c3;
+      // lane l owns bins 255-4l .. 252-4l (summed over the copies); find the
+      // bin holding the need_r-th largest digit, scanning from the top
+      uint32_t c[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int cp = 0; cp < kHistCopies; ++cp) c[j] += hist[cp * 256 + 255 - 4 * lane - j];
+      const uint32_t s = c[0] + c[1] + c[2] + c[3];
       uint32_t incl = s;
 #pragma unroll
       for (int off = 1; off < kWave; off <<= 1) {
@@ -134,18 +136,10 @@ __device__ __forceinline__ void radix_select(ForKeys for_keys, uint32_t m, uint3
       }
       const uint32_t excl = incl - s;
       if (excl < need_r && need_r <= incl) {
-        uint32_t cum = excl, d;
-        if (need_r <= cum + c0) {
-          d = 255 - 4 * lane;
-        } else if (cum += c0, need_r <= cum + c1) {
-          d = 254 - 4 * lane;
-        } else if (cum += c1, need_r <= cum + c2) {
-          d = 253 - 4 * lane;
-        } else {
-          cum += c2;
-          d = 252 - 4 * lane;
-        }
-        sh.digit = d;
+        uint32_t cum = excl;
+        int j = 0;
+        while (j < 3 && need_r > cum + c[j]) cum += c[j++];
+        sh.digit = 255 - 4 * lane - j;
         sh.above = cum;
       }
     }
@@ -309,8 +303,8 @@ hipError_t launch_topk_select(const float* scores, int64_t n_sel_rows, int64_t n
     V41_TOPK_REG(256, 8);
   } else if (n_cols <= 256 * 16) {
     V41_TOPK_REG(256, 16);
-  } else if (n_cols <= 256 * 32) {
-    V41_TOPK_REG(256, 32);
+  } else if (n_cols <= 1024 * 8) {
+    V41_TOPK_REG(1024, 8);
   } else if (n_cols <= 1024 * 32) {
     V41_TOPK_REG(1024, 32);
   } else {
