@@ -366,8 +366,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(Params p) {
 // without partial results.  The workgroups of one row set sit 8 apart in the
 // grid (one XCD under round-robin dispatch) and share its rows in that L2.
 // Eight wavefronts (two per SIMD, so one hides the other's latencies) each
-// work alone on every eighth 16-row tile with their own online softmax, and
-// are merged at the end:
+// work alone on 16-row tiles handed out by an LDS counter, with their own
+// online softmax, and are merged at the end:
 //  * the 16 heads' queries sit in LDS and feed the QK B operand;
 //  * a lane loads its 16 x 16 bytes of a tile straight into the layout of the
 //    QK A operand, one tile ahead;
@@ -468,6 +468,7 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
   __shared__ uint32_t wave_cnt[kW];
   __shared__ float xm[kW][kNarrowHeads];
   __shared__ float xl[kW][kNarrowHeads];
+  __shared__ uint32_t tile_ctr;  // next tile to hand out
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -486,7 +487,8 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
   const int64_t total_rows = p.rows_a_len + p.rows_b_len;
 
   // ---- the 16 heads' queries into LDS (zero rows past n_heads); the
-  // compaction's barriers publish them
+  // compaction's barriers publish them and the tile counter
+  if (tid == 0) tile_ctr = 0u;
   {
     constexpr int CPR = D / 8;
     const uint16_t* q0 = p.q + (qi * p.n_heads + hg * kNarrowHeads) * D;
@@ -503,15 +505,21 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
   const int tps = (n_tiles + p.splits - 1) / p.splits;
   const int t_begin = split * tps;
   const int t_end = (t_begin + tps < n_tiles) ? t_begin + tps : n_tiles;
-  // this wavefront's tiles: t_begin + wave + kW i
-  const int nw = (t_begin + wave < t_end) ? (t_end - t_begin - wave + kW - 1) / kW : 0;
+  const int nt = t_end > t_begin ? t_end - t_begin : 0;
+  // tiles go to whichever wavefront asks next (the second wavefront of a
+  // SIMD gets fewer issue slots, so a fixed deal leaves it behind)
+  auto grab = [&]() -> int {
+    uint32_t t = 0u;
+    if (lane == 0) t = atomicAdd(&tile_ctr, 1u);
+    return (int)__builtin_amdgcn_readfirstlane(t);
+  };
 
   // ---- a lane's share of a tile: row r16, chunks 4kk + g (rows past n_valid
   // repeat the first valid row: finite data, probability 0)
   const uint16_t* a_base = p.rows_a + b * p.a_bs;
   const uint16_t* b_base = p.rows_b + b * p.b_bs;
   auto load = [&](int i, u32x4 (&rb)[KS]) {
-    int pos = (t_begin + wave + kW * i) * kWaveRows + r16;
+    int pos = (t_begin + i) * kWaveRows + r16;
     if ((uint32_t)pos >= n_valid) pos = 0;
     const int64_t ix = list[pos];
     const uint16_t* src =
@@ -538,8 +546,10 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
       slot + tr_row * WS::kStride + 16 * ((tq >> 1) ^ WS::swz(tr_row)) + 8 * (tq & 1));
 
   u32x4 rb[KS];
-  if (nw > 0) load(0, rb);
-  for (int i = 0; i < nw; ++i) {
+  int cur = grab();
+  if (cur < nt) load(cur, rb);
+  while (cur < nt) {
+    const int nxt = grab();
     // S^T: rows 4g + e of the tile, head r16
     f32x4 sa[4];
 #pragma unroll
@@ -552,9 +562,9 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
     const f32x4 sacc = (sa[0] + sa[1]) + (sa[2] + sa[3]);
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) *reinterpret_cast<u32x4*>(slot + st_off + 64 * kk) = rb[kk];
-    if (i + 1 < nw) load(i + 1, rb);
+    if (nxt < nt) load(nxt, rb);
 
-    const int rbase = (t_begin + wave + kW * i) * kWaveRows + 4 * g;
+    const int rbase = (t_begin + cur) * kWaveRows + 4 * g;
     float sv[4];
     float mx = kNegInf;
 #pragma unroll
@@ -598,6 +608,7 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
 #pragma unroll
       for (int j = 0; j < DT; ++j) acc_o[j] = mfma16x16x16(t[j], pk, acc_o[j]);
     }
+    cur = nxt;
   }
 
   // ---- merge the wavefronts: M = max m_w, O = sum 2^(m_w - M) O_w,
