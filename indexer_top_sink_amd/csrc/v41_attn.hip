@@ -176,12 +176,66 @@ __device__ __forceinline__ uint32_t compact_idx(const int32_t* __restrict__ irow
   return n_valid;
 }
 
+// One 32-row tile of the wide form into the LDS buffer dst: rows
+// base_pos .. base_pos+31 of the compacted list (rows past n_valid repeat the
+// first valid row: finite data whose probability is 0).  For D = 512 each
+// wavefront's eight row indices come from one LDS read and go to the row
+// loads by readlane.  (A function template rather than a lambda: the host
+// pass drops kernels whose lambdas hold discarded constexpr branches.)
+// 16 bytes per lane from src into LDS at dst + 16 lane (global_load_lds_dwordx4).
+__device__ __forceinline__ void dma16(const uint16_t* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)(size_t)dst, 16, 0, 0);
+}
+
+__device__ __forceinline__ int lane_value(int v, int j) { return __builtin_amdgcn_readlane(v, j); }
+
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_kernel(Params p) {
+__device__ __forceinline__ void wide_gather(uint8_t* dst, int base_pos, const int32_t* list,
+                                            uint32_t n_valid, int wave, int lane,
+                                            const uint16_t* a_base, const uint16_t* b_base,
+                                            int64_t rows_a_len) {
+  using TL = Tile<D, kTile>;
+  constexpr int kW = kThreads / kWave;
+  if constexpr (TL::RPI == 1) {
+    constexpr int kPer = TL::kBlocks / kW;
+    int pos = base_pos + wave + kW * (lane % kPer);
+    if ((uint32_t)pos >= n_valid) pos = 0;
+    const int32_t my_ix = list[pos];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int bk = wave + kW * j;
+      const int64_t ix = lane_value(my_ix, j);
+      const uint16_t* src = (ix < rows_a_len) ? a_base + ix * D : b_base + (ix - rows_a_len) * D;
+      dma16(src + 8 * (lane ^ TL::swz(bk)), dst + bk * TL::kBlkBytes);
+    }
+  } else {
+#pragma unroll
+    for (int bk = wave; bk < TL::kBlocks; bk += kW) {
+      const int r = bk * TL::RPI + lane / TL::LPR;
+      const int c = (lane % TL::LPR) ^ TL::swz(r);
+      int pos = base_pos + r;
+      if ((uint32_t)pos >= n_valid) pos = 0;
+      const int64_t ix = list[pos];
+      const uint16_t* src = (ix < rows_a_len) ? a_base + ix * D : b_base + (ix - rows_a_len) * D;
+      dma16(src + 8 * c, dst + bk * TL::kBlkBytes);
+    }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// NS: LDS ring depth in tiles (NS - 1 tiles in flight ahead of the one in use).
+template <int D, int NS>
+__global__ __launch_bounds__(kThreads, NS == 2 ? 2 : 1) void attn_kernel(Params p) {
   using TL = Tile<D, kTile>;
   constexpr int KS = D / 32;  // QK K-steps
   constexpr int MT = D / 16;  // PV M-tiles (dims)
-  __shared__ __attribute__((aligned(16))) uint8_t tiles[2 * TL::kBufBytes];
+  constexpr int kPerWave = TL::kBlocks / (kThreads / kWave);  // loads per tile and wavefront
+  static_assert(NS >= 2 && NS <= 4, "ring depth");
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[NS * TL::kBufBytes];
   __shared__ int32_t list[kMaxWidth];
   __shared__ uint32_t wave_cnt[kThreads / kWave];
 
@@ -204,28 +258,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(Params p) {
   const int t_begin = split * tps;
   const int t_end = (t_begin + tps < n_tiles) ? t_begin + tps : n_tiles;
 
-  // ---- gather of one tile into LDS buffer `buf` (rows past n_valid repeat
-  // the first valid row: finite data whose probability is 0)
   const uint16_t* a_base = p.rows_a + b * p.a_bs;
   const uint16_t* b_base = p.rows_b + b * p.b_bs;
-  auto gather = [&](int tile, int buf) {
-    const int base_pos = tile * kTile;
-#pragma unroll
-    for (int bk = wave; bk < TL::kBlocks; bk += kThreads / kWave) {
-      const int r = bk * TL::RPI + lane / TL::LPR;
-      const int c = (lane % TL::LPR) ^ TL::swz(r);
-      int pos = base_pos + r;
-      if ((uint32_t)pos >= n_valid) pos = 0;
-      int64_t ix = list[pos];
-      if (TL::RPI == 1) ix = __builtin_amdgcn_readfirstlane((int)ix);
-      const uint16_t* src = (ix < p.rows_a_len) ? a_base + ix * D
-                                                : b_base + (ix - p.rows_a_len) * D;
-      __builtin_amdgcn_global_load_lds(
-          src + 8 * c, (lds_void*)(size_t)(tiles + buf * TL::kBufBytes + bk * TL::kBlkBytes),
-          16, 0, 0);
-    }
-  };
-
   // ---- query fragments (B operand of S^T = G Q^T): head r16, dims 32kk+8g..
   bf16x8 qf[KS];
   {
@@ -260,12 +294,29 @@ __global__ __launch_bounds__(kThreads, 2) void attn_kernel(Params p) {
   const int tr_lo = TL::row_off(r_lo) + 16 * ((tb >> 1) ^ TL::swz(r_lo)) + 8 * (tb & 1);
   const int tr_hi = TL::row_off(r_hi) + 16 * ((tb >> 1) ^ TL::swz(r_hi)) + 8 * (tb & 1);
 
-  if (t_begin < t_end) gather(t_begin, 0);
-  for (int tile = t_begin; tile < t_end; ++tile) {
-    const int buf = (tile - t_begin) & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // the query loads land before the ring's loads go out, so the waits below
+  // count ring loads only (each empty asm makes the compiler wait here)
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) asm volatile("" : "+v"(qf[kk]));
+  asm volatile("" ::"v"(sink2));
+  const int nt = t_end > t_begin ? t_end - t_begin : 0;
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < nt)
+      wide_gather<D>(tiles + st * TL::kBufBytes, (t_begin + st) * kTile, list, n_valid, wave,
+                     lane, a_base, b_base, p.rows_a_len);
+  for (int k = 0; k < nt; ++k) {
+    const int tile = t_begin + k;
+    const int buf = k % NS;
+    // tiles issued after this one: min(NS - 2, nt - 1 - k)
+    const int ahead = (nt - 1 - k < NS - 2) ? nt - 1 - k : NS - 2;
+    if (ahead <= 0) wait_vm<0>();
+    else if (ahead == 1) wait_vm<kPerWave>();
+    else wait_vm<2 * kPerWave>();
     lds_barrier();
-    if (tile + 1 < t_end) gather(tile + 1, buf ^ 1);
+    if (k + NS - 1 < nt)
+      wide_gather<D>(tiles + ((k + NS - 1) % NS) * TL::kBufBytes, (tile + NS - 1) * kTile, list,
+                     n_valid, wave, lane, a_base, b_base, p.rows_a_len);
     const uint8_t* tb_base = tiles + buf * TL::kBufBytes;
 
     // S^T tile: rows 16mt + 4g + i, head r16
@@ -746,9 +797,11 @@ hipError_t launch_d(const AttnArgs& a, int splits, hipStream_t s) {
     hipLaunchKernelGGL((attn_narrow_kernel<D>), dim3((unsigned)blocks), dim3(kNarrowThreads), 0,
                        s, p, hg, units);
   } else {
+    // two workgroups per CU with a two-tile ring each (a four-tile ring with
+    // one workgroup per CU measured slower on row-split decode shapes)
     const dim3 grid((unsigned)(nq * splits), (unsigned)((a.n_heads + kHeadsPerBlock - 1) /
                                                         kHeadsPerBlock));
-    hipLaunchKernelGGL((attn_kernel<D>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((attn_kernel<D, 2>), grid, dim3(kThreads), 0, s, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
