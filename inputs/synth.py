@@ -215,6 +215,17 @@ def uniform_f32(seed: int, tag: int, shape, scale: float = 1.0) -> np.ndarray:
     return (uniform(seed, tag, n) * scale).astype(np.float32).reshape(shape)
 
 
+def unit_pairs_f32(seed: int, tag: int, shape) -> np.ndarray:
+    """f32 [*shape, 2]: random points of the unit circle (a normal pair divided
+    by its length in double, then rounded to binary32), for tests of a rotation
+    with an arbitrary table."""
+    n = int(np.prod(shape))
+    z = normal(seed, tag, 2 * n).reshape(n, 2)
+    r = np.hypot(z[:, 0], z[:, 1])
+    r[r == 0.0] = 1.0
+    return (z / r[:, None]).astype(np.float32).reshape(tuple(shape) + (2,))
+
+
 def bernoulli_u8(seed: int, tag: int, shape, p: float = 0.5) -> np.ndarray:
     n = int(np.prod(shape))
     return (uniform(seed, tag, n) < p).astype(np.uint8).reshape(shape)

@@ -55,6 +55,11 @@ def lib():
                                           C.c_int32, f32p, C.c_double, C.c_int32, C.c_int32,
                                           u16p]
         L.ora_sparse_attn_one.restype = C.c_int
+        L.ora_rope_table.argtypes = [C.c_double, C.c_int32, C.c_int64, f32p]
+        L.ora_rope_table.restype = C.c_int
+        L.ora_rope_rows.argtypes = [u16p, u16p, C.c_int64, C.c_int32, C.c_int32, f32p,
+                                    C.POINTER(C.c_int64), C.c_int32]
+        L.ora_rope_rows.restype = C.c_int
         _lib = L
     return _lib
 
@@ -238,3 +243,45 @@ def scores_to_f32(s: np.ndarray) -> np.ndarray:
     """Oracle scores rounded once to binary32 (the precision the scores are
     handed over in)."""
     return np.asarray(s, dtype=np.float64).astype(np.float32)
+
+
+# ---------------------------------------------------------------- RoPE
+def rope_table(theta: float, rope_dim: int, n_pos: int) -> np.ndarray:
+    """f32 [n_pos, rope_dim/2, 2]: (cos, sin) of p * theta^(-2i/rope_dim),
+    each rounded once to binary32 (freqs_cis at ratio 0)."""
+    out = np.empty((n_pos, rope_dim // 2, 2), dtype=np.float32)
+    rc = lib().ora_rope_table(float(theta), rope_dim, n_pos, _p(out, C.c_float))
+    if rc != 0:
+        raise ValueError("rope_dim must be even and positive, theta positive")
+    return out
+
+
+def rope_rows(x: np.ndarray, table: np.ndarray, row_pos, rope_dim: int,
+              inverse: bool = False) -> np.ndarray:
+    """bf16 rows [..., row_len] (uint16 bits): the last rope_dim values of row
+    r rotated by table[row_pos[r]] (negated angle when inverse), binary32
+    products, bf16 results; row_pos has one entry per row of the flattened
+    leading axes."""
+    x = _c(x, np.uint16)
+    row_len = x.shape[-1]
+    rows = x.size // row_len
+    pos = _c(np.asarray(row_pos).reshape(-1), np.int64)
+    if pos.shape[0] != rows:
+        raise ValueError("one position per row")
+    tab = _c(table, np.float32)
+    if pos.size and (pos.min() < 0 or pos.max() >= tab.shape[0]):
+        raise ValueError("position outside the table")
+    if tab.ndim != 3 or tab.shape[1] * 2 != rope_dim or tab.shape[2] != 2:
+        raise ValueError("table must be [n_pos, rope_dim/2, 2]")
+    out = np.empty_like(x)
+    rc = lib().ora_rope_rows(_p(x, C.c_uint16), _p(out, C.c_uint16), rows, row_len, rope_dim,
+                             _p(tab, C.c_float), _p(pos, C.c_int64), 1 if inverse else 0)
+    if rc != 0:
+        raise ValueError("rope_dim must be even, positive and at most row_len")
+    return out
+
+
+def rope_fp8_rows(x: np.ndarray, table: np.ndarray, row_pos, rope_dim: int) -> np.ndarray:
+    """The window-key epilogue: RoPE on the last rope_dim values (bf16 out),
+    then the fp8 round trip of the whole row (W_{t,448:} <- R_t w; W <- FP8(W))."""
+    return fp8_round_rows(rope_rows(x, table, row_pos, rope_dim))

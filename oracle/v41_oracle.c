@@ -1,7 +1,9 @@
 /*
  * Plain CPU oracle for the hot path of DeepSeek-V4.1 compressed sparse
  * attention: the fp8 round trip of kv rows, the window selection, the indexer
- * score, the index top-k and the sparse attention with a per-head sink.
+ * score, the index top-k and the sparse attention with a per-head sink, and
+ * the rotary embedding (its table and the rotation) that the kv rows and the
+ * queries go through before the path.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * CPU-baseline leg of the benchmark may load this library.  The GPU library
@@ -11,12 +13,15 @@
  *
  * Sources (the pages this follows):
  *  - "deepseek_v41_ref::attn" rustdoc, module description and the function
- *    contracts act_quant_inplace, pow2_ceil, window_topk_idxs, sparse_attn
- *    (precision contract; ring-cache example).
+ *    contracts act_quant_inplace, pow2_ceil, window_topk_idxs, sparse_attn,
+ *    apply_rotary, freqs_cis (precision contract; ring-cache example).
  *  - "Compressed sparse attention" layer page (atlas, reindex layer,
  *    p=1000), section "All 25 steps": the FP8(W) step, the indexer score
- *    S^I, the top-512 selection I_t, the window set J^w_t, the join Y/J/G_t
- *    and the sink softmax A and O.
+ *    S^I, the top-512 selection I_t, the window set J^w_t, the join Y/J/G_t,
+ *    the sink softmax A and O, and the rotations R_t (queries, window keys)
+ *    and R_t^-1 (output); the model code and config shown on that page
+ *    (RoPE on the last rope_head_dim = 64 values, rope_theta = 10000 at
+ *    ratio 0).
  *  - "attn_v41.rs" source page, module documentation (selection width
  *    limit, -1 = absent, indices offset past the window rows) and the
  *    AttnV41Run struct (q after RoPE, rows_a / rows_b, idx layout).
@@ -34,6 +39,8 @@
  *  - The softmax subtracts m = max(sink_h, max_i s_i) before exp: the
  *    result is the same real number, it only avoids overflow of exp.
  *  - Index values outside [0, rows_a_len + rows_b_len) are skipped like -1.
+ *  - The RoPE table is cos/sin of p * theta^(-2i/rope_dim), rounded once to
+ *    binary32; the rotation's binary32 products are not fused.
  */
 #include <math.h>
 #include <stdint.h>
@@ -427,5 +434,95 @@ int ora_sparse_attn_one(const uint16_t *q, const uint16_t *rows_a,
     }
     free(wts);
     free(acc);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* rotary position embedding (apply_rotary, freqs_cis; R_t, R_t^-1)    */
+/* ------------------------------------------------------------------ */
+
+/*
+ * The RoPE table at ratio 0 ("deepseek_v41_ref::attn" rustdoc, freqs_cis:
+ * [seqlen][dim/2] pairs (cos, sin), no YaRN; base rope_theta = 10000 in the
+ * config shown on the "Compressed sparse attention" layer page).
+ *
+ * Reading (the pages name the table and its shape, not its formula): pair i
+ * of position p holds the cosine and sine of the angle p * theta^(-2i/dim),
+ * the usual rotary frequency ladder, pair 0 turning fastest.  Each entry is
+ * the real number rounded once to binary32; it is evaluated in long double
+ * (64-bit significand) so that the one rounding to binary32 is the only one
+ * that matters.
+ *
+ * table: [n_pos][rope_dim / 2][2] floats.  Returns 0, or -1 for an odd or
+ * non-positive rope_dim or a non-positive theta.
+ */
+int ora_rope_table(double theta, int32_t rope_dim, int64_t n_pos, float *table)
+{
+    if (rope_dim <= 0 || rope_dim % 2 != 0 || !(theta > 0.0))
+        return -1;
+    int32_t half = rope_dim / 2;
+    for (int32_t i = 0; i < half; ++i) {
+        long double expo = -(long double)(2 * i) / (long double)rope_dim;
+        long double freq = powl((long double)theta, expo);
+        for (int64_t p = 0; p < n_pos; ++p) {
+            long double ang = (long double)p * freq;
+            table[(p * half + i) * 2 + 0] = (float)cosl(ang);
+            table[(p * half + i) * 2 + 1] = (float)sinl(ang);
+        }
+    }
+    return 0;
+}
+
+/*
+ * Rotate the last rope_dim values of each row ("deepseek_v41_ref::attn"
+ * rustdoc, apply_rotary; "Compressed sparse attention", All 25 steps:
+ * Q_{...,448:} <- R_t Q, W_{t,448:} <- R_t w^n, and the inverse R_t^-1 on O).
+ *
+ * The rotated part is read as rope_dim/2 complex numbers, element 2i the
+ * real part and element 2i+1 the imaginary part of number i; number i is
+ * multiplied by table[pos][i] = cos + i sin (by cos - i sin when inverse is
+ * set: the negated angle).  The product is taken in binary32, as the
+ * precision paragraph of the same page fixes:
+ *     re = x0*c - x1*s,   im = x0*s + x1*c
+ * with each product and each sum rounded to binary32 (no fused
+ * multiply-add; reading: the pages fix the precision, not the order), and
+ * each result rounded once to bf16.  Values before the rotated part are
+ * copied.
+ *
+ * in, out: [rows][row_len] bf16 (may be the same buffer); row r is at
+ * position row_pos[r]; table: [..][rope_dim/2][2].  Returns 0, or -1 for a
+ * rope_dim that is odd, non-positive or larger than row_len.
+ */
+int ora_rope_rows(const uint16_t *in, uint16_t *out, int64_t rows,
+                  int32_t row_len, int32_t rope_dim, const float *table,
+                  const int64_t *row_pos, int32_t inverse)
+{
+    if (rope_dim <= 0 || rope_dim % 2 != 0 || rope_dim > row_len)
+        return -1;
+    int32_t half = rope_dim / 2;
+    int32_t start = row_len - rope_dim;
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t *x = in + r * (int64_t)row_len;
+        uint16_t *y = out + r * (int64_t)row_len;
+        for (int32_t d = 0; d < start; ++d)
+            y[d] = x[d];
+        const float *tab = table + row_pos[r] * (int64_t)half * 2;
+        for (int32_t i = 0; i < half; ++i) {
+            float c = tab[2 * i + 0];
+            float s = tab[2 * i + 1];
+            if (inverse)
+                s = -s;
+            float x0 = (float)ora_bf16_to_double(x[start + 2 * i]);
+            float x1 = (float)ora_bf16_to_double(x[start + 2 * i + 1]);
+            float a = x0 * c;
+            float b = x1 * s;
+            float re = a - b;
+            float e = x0 * s;
+            float f = x1 * c;
+            float im = e + f;
+            y[start + 2 * i] = ora_double_to_bf16((double)re);
+            y[start + 2 * i + 1] = ora_double_to_bf16((double)im);
+        }
+    }
     return 0;
 }
