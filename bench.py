@@ -15,7 +15,11 @@ a HIP graph per copy and replayed; per-kernel durations come from HIP events
 around graph replays of single kernels on the same stream.  The CPU baseline
 is the oracle (plain C, one thread) on a bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode64]
+With --rope the step starts from q and kv rows before their rotation: q is
+rotated in place and the fp8 call becomes the fused rotation + fp8 + ring write
+(the rotary epilogue); without it that variant is reported as a secondary line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode64] [--rope]
 """
 from __future__ import annotations
 
@@ -97,6 +101,20 @@ def stage_prefill(wl, device, keep_host=False):
     return buf, (d if keep_host else None)
 
 
+def attach_rope(buf, wl, device):
+    """The rotary epilogue's state: the ratio-0 table over every position the
+    step touches, built on the GPU, and (decode) the positions as a device
+    int32 [B] tensor, read on the device by the rotations and the ring write."""
+    import torch
+
+    from indexer_top_sink_amd import layer as LY
+    n_pos = wl.start_pos + wl.n_tokens
+    buf.rope = LY.rope_table(wl.rope_theta, wl.rope_dim, n_pos, device)
+    if wl.mode == "decode":
+        buf.pos_dev = torch.full((wl.batch,), wl.start_pos, dtype=torch.int32, device=device)
+    torch.cuda.synchronize()
+
+
 def clone_buffers(buf):
     """Another copy of every tensor of a buffer set (same values)."""
     import copy
@@ -110,9 +128,10 @@ def clone_buffers(buf):
 
 
 # ----------------------------------------------------------------- the steps
-def step_calls(buf, mode):
-    """The five calls of one step as separate closures (kernel order)."""
-    from indexer_top_sink_amd import layer as LY
+def step_calls(buf, mode, rope=False):
+    """The five calls of one step as separate closures (kernel order).  With
+    rope, q is rotated in place first and the fp8 call becomes the fused
+    rotation + fp8 + ring write of the kv rows."""
     from indexer_top_sink_amd import v41
     g = buf.geo
     D, W = g.head_dim, g.window
@@ -120,9 +139,20 @@ def step_calls(buf, mode):
         B, L, width, pos = buf.batch, buf.n_rows, buf.width, buf.pos
         slot = pos % W
         ws_bytes = buf.workspace.numel() if buf.workspace is not None else 0
-        return [
-            ("fp8_round_rows", lambda: v41.v41_fp8_round_rows(
-                buf.kv_new, D, buf.ring.data_ptr() + 2 * slot * D, W * D, B, D)),
+        if rope:
+            rt = buf.rope
+            first = [
+                ("rope_rows", lambda: v41.v41_rope_rows(
+                    buf.q, D, buf.q, D, B, 1, g.n_heads, D, rt.rope_dim, rt.table, rt.n_pos,
+                    buf.pos_dev, pos, 0)),
+                ("rope_fp8_rows", lambda: v41.v41_rope_fp8_rows(
+                    buf.kv_new, D, None, D, B, 1, D, rt.rope_dim, rt.table, rt.n_pos,
+                    buf.pos_dev, pos, buf.ring, W, W * D)),
+            ]
+        else:
+            first = [("fp8_round_rows", lambda: v41.v41_fp8_round_rows(
+                buf.kv_new, D, buf.ring.data_ptr() + 2 * slot * D, W * D, B, D))]
+        return first + [
             ("window_idx", lambda: v41.v41_window_idx(pos, 1, W, B, buf.idx, width, width)),
             ("indexer_scores", lambda: v41.v41_indexer_scores(
                 buf.qI, buf.kI, L * g.index_dim, buf.w, None, 0, 1, B, 1, pos, g.ratio,
@@ -135,9 +165,20 @@ def step_calls(buf, mode):
         ]
     T, L, width, cols = buf.n_tokens, buf.n_rows, buf.width, buf.cols
     cw = buf.cand.shape[1] if buf.cand is not None else 0
-    return [
-        ("fp8_round_rows", lambda: v41.v41_fp8_round_rows(
-            buf.kv_chunk, D, buf.rows_a, D, T, D, buf.ring, W, 0)),
+    if rope:
+        rt = buf.rope
+        first = [
+            ("rope_rows", lambda: v41.v41_rope_rows(
+                buf.q, D, buf.q, D, 1, T, g.n_heads, D, rt.rope_dim, rt.table, rt.n_pos, None,
+                0, 0)),
+            ("rope_fp8_rows", lambda: v41.v41_rope_fp8_rows(
+                buf.kv_chunk, D, buf.rows_a, D, 1, T, D, rt.rope_dim, rt.table, rt.n_pos, None,
+                0, buf.ring, W, 0)),
+        ]
+    else:
+        first = [("fp8_round_rows", lambda: v41.v41_fp8_round_rows(
+            buf.kv_chunk, D, buf.rows_a, D, T, D, buf.ring, W, 0))]
+    return first + [
         ("window_idx", lambda: v41.v41_window_idx(0, T, W, 1, buf.idx, width, T * width)),
         ("indexer_scores", lambda: v41.v41_indexer_scores(
             buf.qI, buf.kI, L * g.index_dim, buf.w, buf.cand, cw, buf.cand_block, 1, T, 0,
@@ -181,10 +222,12 @@ def time_replays(graphs, reps, torch):
 
 
 # ----------------------------------------------------------------- algorithmic work
-def algorithmic(wl, host_idx=None, valid_pairs=None):
+def algorithmic(wl, host_idx=None, valid_pairs=None, rope=False):
     """Bytes and flops per kernel of one step (what the method must move or
     compute).  Attention flops count 4 * H * D per valid index entry; indexer
-    flops 2 * HI * DI per visible (query, position) pair."""
+    flops 2 * HI * DI per visible (query, position) pair.  The rotary
+    epilogue moves the rotated tail of every q head in place, one table row
+    per position, and the kv rows in and out (plus the ring copy)."""
     H, D, HI, DI, W = wl.n_heads, wl.head_dim, wl.index_heads, wl.index_dim, wl.window
     Q, L = wl.queries, wl.n_rows
     if wl.mode == "decode":
@@ -210,6 +253,15 @@ def algorithmic(wl, host_idx=None, valid_pairs=None):
         rows_bytes = (wl.n_tokens + L) * D * 2   # every row source read once
     k["sparse_attn_sink"] = {"bytes": rows_bytes + Q * wl.width * 4 + 2 * Q * H * D * 2,
                              "flops": idx_valid * 4 * H * D}
+    if rope:
+        rd = wl.rope_dim
+        table = Q * rd // 2 * 8      # one table row per distinct position
+        del k["fp8_round_rows"]
+        k["rope_rows"] = {"bytes": Q * H * rd * 2 * 2 + table, "flops": 0}
+        ring_rows = min(wl.n_tokens, wl.window) * wl.batch
+        kv_out = fp8_rows if wl.mode == "prefill" else 0   # decode writes the ring only
+        k["rope_fp8_rows"] = {"bytes": fp8_rows * D * 2 + (kv_out + ring_rows) * D * 2 + table,
+                              "flops": 0}
     return k
 
 
@@ -250,8 +302,7 @@ def cpu_baseline(wl, n_sample, budget_s=30.0):
 
 
 # ----------------------------------------------------------------- main
-def run_workload(name, steps, warmup, n_sets, torch, device):
-    from indexer_top_sink_amd import layer as LY
+def run_workload(name, steps, warmup, n_sets, torch, device, rope=False):
     wl = WL.WORKLOADS[name]
     t0 = time.time()
     if wl.mode == "decode":
@@ -259,12 +310,14 @@ def run_workload(name, steps, warmup, n_sets, torch, device):
         buf0.pos = wl.start_pos
     else:
         buf0, _ = stage_prefill(wl, device)
+    if rope:
+        attach_rope(buf0, wl, device)
     sets = [buf0] + [clone_buffers(buf0) for _ in range(n_sets - 1)]
     for s in sets:
         s.pos = getattr(buf0, "pos", 0)
     log(f"{name}: staged {n_sets} input sets in {time.time() - t0:.1f}s")
 
-    calls = [step_calls(s, wl.mode) for s in sets]
+    calls = [step_calls(s, wl.mode, rope) for s in sets]
     # One graph holds one step per input set, as one graph would hold the
     # layers of a model; single-step graphs cover a remainder of K.
     all_graph = capture([f for c in calls for _, f in c], torch)
@@ -284,7 +337,7 @@ def run_workload(name, steps, warmup, n_sets, torch, device):
     e1.record(st)
     e1.synchronize()
     ms_step = e0.elapsed_time(e1) / steps
-    log(f"{name}: {ms_step * 1e3:.1f} us per step")
+    log(f"{name}{' + rope' if rope else ''}: {ms_step * 1e3:.1f} us per step")
 
     # per-kernel durations: a graph of 4 * n_sets launches of one kernel
     # cycling over the input sets, replayed; mean time per launch
@@ -308,7 +361,7 @@ def run_workload(name, steps, warmup, n_sets, torch, device):
             n = min(wl.n_rows, (t + 1) // wl.ratio)
             blocks = np.repeat(cand[t].astype(bool), wl.cand_block)[:n]
             pairs += int(blocks.sum())
-    work = algorithmic(wl, host_idx=idx, valid_pairs=pairs)
+    work = algorithmic(wl, host_idx=idx, valid_pairs=pairs, rope=rope)
     return wl, ms_step, kern_us, work
 
 
@@ -368,6 +421,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode64", choices=sorted(WL.WORKLOADS))
     ap.add_argument("--input-sets", type=int, default=3)
+    ap.add_argument("--rope", action="store_true",
+                    help="make the rotary epilogue (q rotation; kv rotation + fp8 + ring "
+                         "write) part of the timed step")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0)
@@ -397,7 +453,7 @@ def main():
         del src, dst
 
     wl, ms_step, kern_us, work = run_workload(args.workload, args.steps, args.warmup,
-                                              args.input_sets, torch, device)
+                                              args.input_sets, torch, device, rope=args.rope)
     tokens = wl.queries
     value = tokens / (ms_step * 1e-3)
     # the dominant kernel is the one that takes the most time; decode moves
@@ -420,7 +476,7 @@ def main():
                    "head_dim": wl.head_dim, "window": wl.window,
                    "index_heads": wl.index_heads, "index_dim": wl.index_dim,
                    "topk": wl.topk, "ratio": wl.ratio, "hip_graph": True,
-                   "input_sets": args.input_sets},
+                   "input_sets": args.input_sets, "rope_epilogue": bool(args.rope)},
         "roofline": roof,
         "roofline_other": others,
         "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -438,6 +494,17 @@ def main():
                 "indexer_roofline": roofline_entry("indexer_scores", pwork,
                                                    pk["indexer_scores"], "mfma", pw.name),
                 "kernels_us": {k: round(v, 2) for k, v in pk.items()}}}
+    if not args.no_secondary and not args.rope:
+        # the same step with the rotary epilogue in front (pre-rotation q and kv)
+        rw, rms, rk, rwork = run_workload(wl.name, args.steps, args.warmup, args.input_sets,
+                                          torch, device, rope=True)
+        out.setdefault("secondary", {})["with_rope_epilogue"] = {
+            "value": round(rw.queries / (rms * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(rms, 5),
+            "rope_rows": roofline_entry("rope_rows", rwork, rk["rope_rows"], "hbm", rw.name),
+            "rope_fp8_rows": roofline_entry("rope_fp8_rows", rwork, rk["rope_fp8_rows"], "hbm",
+                                            rw.name),
+            "kernels_us": {k: round(v, 2) for k, v in rk.items()}}
     if not args.no_cpu_baseline:
         n = args.cpu_sample or (wl.batch if wl.mode == "decode" else 32)
         t0 = time.time()

@@ -1,7 +1,9 @@
 /*
  * v41.h -- C ABI of the MI355X (gfx950) hot path of DeepSeek-V4.1 compressed
  * sparse attention: fp8 round trip of kv rows, window selection, indexer
- * score, index top-k, and sparse attention with a per-head sink.
+ * score, index top-k, and sparse attention with a per-head sink; the rotary
+ * embedding (table, rotation of queries and output, and the window-key
+ * epilogue rotation + fp8 + ring write) around it.
  *
  * Conventions shared by every call
  *  - bf16 values travel as raw uint16 bit patterns (v41_bf16).
@@ -196,6 +198,82 @@ int v41_sparse_attn_sink(const v41_bf16 *q, const v41_bf16 *rows_a,
 int64_t v41_sparse_attn_workspace_bytes(int32_t batch, int32_t n_tokens,
                                         int32_t n_heads, int32_t head_dim,
                                         int32_t width);
+
+/*
+ * RoPE table at ratio 0 ("deepseek_v41_ref::attn": freqs_cis, the table
+ * without YaRN, [seqlen][dim/2] pairs (cos, sin); rope_theta 10000 in the
+ * config of the "Compressed sparse attention" layer page).
+ *
+ * table[p][i] = (cos a, sin a) with a = p * theta^(-2i / rope_dim) (the usual
+ * rotary frequency ladder: the pages give the table's shape, not its
+ * formula), computed in binary64 and rounded once to binary32.  Entries are
+ * within one binary32 ulp plus 2^-32 of the real values.
+ *
+ *   table    f32 [n_pos][rope_dim / 2][2], 8-byte aligned
+ *   rope_dim positive and even; theta > 0.
+ */
+int v41_rope_table(double theta, int32_t rope_dim, int64_t n_pos, float *table,
+                   v41_stream stream);
+
+/*
+ * Rotation of the last rope_dim values of rows ("deepseek_v41_ref::attn":
+ * apply_rotary; "Compressed sparse attention", All 25 steps:
+ * Q_{...,448:} <- R_t Q on the queries and O_{h,t,448:} <- R_t^-1 O on the
+ * attention output).
+ *
+ * Row r (of batch * n_tokens * rows_per_pos) belongs to sequence
+ * b = r / (n_tokens * rows_per_pos) and token t = (r / rows_per_pos) mod
+ * n_tokens, at position p = (pos ? pos[b] : start_pos) + t.  The rotated part
+ * is read as rope_dim / 2 complex numbers, value 2i the real and 2i+1 the
+ * imaginary part of number i, each multiplied by table[p][i] = c + i s
+ * (by c - i s when inverse != 0): re = x0*c - x1*s and im = x0*s + x1*c with
+ * every product and sum rounded to binary32 (no fused multiply-add), then
+ * rounded to bf16.  Values before the rotated part are copied.
+ *
+ *   in, out  bf16 [rows][in_ld], [rows][out_ld]; out == in (same ld) rotates
+ *            in place and then touches only the rotated part; otherwise the
+ *            two must not overlap.  For queries [B*T][H][D]: rows_per_pos = H,
+ *            row_len = in_ld = D.
+ *   row_len  multiple of 8; rope_dim a multiple of 8, <= row_len
+ *   table    f32 [table_rows][rope_dim / 2][2] (v41_rope_table's layout)
+ *   pos      device int32 [batch] or NULL; with NULL, start_pos .. start_pos +
+ *            n_tokens - 1 must lie in the table.  A row whose position falls
+ *            outside [0, table_rows) (only possible through pos) is not
+ *            written.
+ *   in, out, table, pos: 16-byte aligned.
+ */
+int v41_rope_rows(const v41_bf16 *in, int64_t in_ld, v41_bf16 *out, int64_t out_ld,
+                  int32_t batch, int32_t n_tokens, int32_t rows_per_pos, int32_t row_len,
+                  int32_t rope_dim, const float *table, int64_t table_rows,
+                  const int32_t *pos, int64_t start_pos, int32_t inverse,
+                  v41_stream stream);
+
+/*
+ * The window-key epilogue in one pass: the rotation of v41_rope_rows on the
+ * last rope_dim values (bf16 result), then the fp8 round trip of
+ * v41_fp8_round_rows on the whole row, then the ring write ("Compressed
+ * sparse attention", All 25 steps: W_{t,448:} <- R_t w^n_{t,448:}, then
+ * W <- FP8(W); "deepseek_v41_ref::attn": the attention forward writes the new
+ * kv rows into the cache's ring; "attn_v41.rs": the captured decode step's
+ * ring_put takes the slot pos[0] mod window on the device).
+ *
+ * Row r = b * n_tokens + t is token t of sequence b at position
+ * p = (pos ? pos[b] : start_pos) + t (one row per position: rows_per_pos 1).
+ *
+ *   out      bf16 [batch * n_tokens][out_ld] or NULL (ring only, as at a
+ *            decode where the ring is the only home of the new row)
+ *   ring     bf16 ring of sequence b at ring + b * ring_bs, [ring_slots]
+ *            [row_len], or NULL; each of the last min(n_tokens, ring_slots)
+ *            tokens of a sequence is also written to slot p mod ring_slots.
+ *            The ring must not overlap in.
+ *   row_len  multiple of 32 (the fp8 block); other arguments as for
+ *            v41_rope_rows.  At least one of out and ring is given.
+ */
+int v41_rope_fp8_rows(const v41_bf16 *in, int64_t in_ld, v41_bf16 *out, int64_t out_ld,
+                      int32_t batch, int32_t n_tokens, int32_t row_len, int32_t rope_dim,
+                      const float *table, int64_t table_rows, const int32_t *pos,
+                      int64_t start_pos, v41_bf16 *ring, int32_t ring_slots,
+                      int64_t ring_bs, v41_stream stream);
 
 #ifdef __cplusplus
 }

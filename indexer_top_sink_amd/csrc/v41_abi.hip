@@ -11,6 +11,7 @@
 
 #include "../../include/v41.h"
 #include "v41_common.h"
+#include "v41_rope.h"
 
 namespace {
 
@@ -62,7 +63,7 @@ extern "C" {
 
 const char* v41_last_error(void) { return g_err; }
 
-int v41_abi_version(void) { return 1; }
+int v41_abi_version(void) { return 2; }
 
 int v41_fp8_round_rows(const v41_bf16* in, int64_t in_ld, v41_bf16* out, int64_t out_ld,
                        int64_t rows, int32_t row_len, v41_bf16* ring, int32_t ring_slots,
@@ -239,6 +240,119 @@ int v41_sparse_attn_sink(const v41_bf16* q, const v41_bf16* rows_a, int64_t rows
   a.workspace = workspace;
   a.workspace_bytes = workspace ? workspace_bytes : 0;
   return launched(v41::launch_sparse_attn_sink(a, (hipStream_t)stream), "sparse_attn_sink");
+}
+
+int v41_rope_table(double theta, int32_t rope_dim, int64_t n_pos, float* table,
+                   v41_stream stream) {
+  if (!(theta > 0.0) || !(theta < 1e300))
+    return fail(V41_EINVAL, "rope_table: theta must be positive and finite");
+  if (rope_dim <= 0 || rope_dim % 2 != 0)
+    return fail(V41_EINVAL, "rope_table: rope_dim %d is not a positive even number", rope_dim);
+  if (n_pos < 0) return fail(V41_EINVAL, "rope_table: n_pos < 0");
+  if (n_pos > 0 && table == nullptr) return fail(V41_EINVAL, "rope_table: NULL table");
+  if ((reinterpret_cast<uintptr_t>(table) & 7u) != 0)
+    return fail(V41_EINVAL, "rope_table: table must be 8-byte aligned");
+  if (n_pos > (int64_t)1 << 40) return fail(V41_EINVAL, "rope_table: n_pos too large");
+  int rc = check_device();
+  if (rc) return rc;
+  return launched(v41::launch_rope_table(theta, rope_dim, n_pos, table, (hipStream_t)stream),
+                  "rope_table");
+}
+
+namespace {
+
+// Checks shared by the two rotation entry points.
+int check_rope_rows(const char* who, const v41_bf16* in, int64_t in_ld, const v41_bf16* out,
+                    int64_t out_ld, int32_t batch, int32_t n_tokens, int32_t rows_per_pos,
+                    int32_t row_len, int32_t rope_dim, const float* table, int64_t table_rows,
+                    const int32_t* pos, int64_t start_pos, int32_t row_quantum) {
+  if (batch < 0 || n_tokens < 0) return fail(V41_EINVAL, "%s: negative batch/n_tokens", who);
+  if (rows_per_pos < 1) return fail(V41_EINVAL, "%s: rows_per_pos < 1", who);
+  if (row_len <= 0 || row_len % row_quantum != 0)
+    return fail(V41_EINVAL, "%s: row_len %d is not a positive multiple of %d", who, row_len,
+                row_quantum);
+  if (rope_dim <= 0 || rope_dim % 8 != 0 || rope_dim > row_len)
+    return fail(V41_EINVAL, "%s: rope_dim %d must be a positive multiple of 8, at most row_len",
+                who, rope_dim);
+  if (in_ld < row_len || in_ld % 8 != 0 || (out != nullptr && (out_ld < row_len ||
+                                                               out_ld % 8 != 0)))
+    return fail(V41_EINVAL, "%s: in_ld/out_ld must be >= row_len and multiples of 8", who);
+  const int64_t rows = (int64_t)batch * n_tokens * rows_per_pos;
+  if (rows * (row_len / 8) >= 0x7FFFFFFFLL)
+    return fail(V41_EINVAL, "%s: rows * row_len / 8 must stay below 2^31", who);
+  if (rows > 0 && (in == nullptr || table == nullptr))
+    return fail(V41_EINVAL, "%s: NULL in or table", who);
+  if (!aligned16(in) || !aligned16(out) || !aligned16(table) || !aligned16(pos))
+    return fail(V41_EINVAL, "%s: pointers must be 16-byte aligned", who);
+  if (table_rows < 1) return fail(V41_EINVAL, "%s: table_rows < 1", who);
+  if (pos == nullptr && (start_pos < 0 || start_pos + n_tokens > table_rows))
+    return fail(V41_EINVAL, "%s: positions %lld .. %lld outside the table's %lld rows", who,
+                (long long)start_pos, (long long)(start_pos + n_tokens - 1),
+                (long long)table_rows);
+  if (in != nullptr && out != nullptr && in != out) {
+    // distinct buffers must not overlap (in place means the same pointer)
+    const char* a0 = reinterpret_cast<const char*>(in);
+    const char* b0 = reinterpret_cast<const char*>(out);
+    const int64_t span_in = ((rows - 1) * in_ld + row_len) * 2;
+    const int64_t span_out = ((rows - 1) * out_ld + row_len) * 2;
+    if (rows > 0 && a0 < b0 + span_out && b0 < a0 + span_in)
+      return fail(V41_EINVAL, "%s: in and out overlap without being the same buffer", who);
+  }
+  if (in != nullptr && in == out && in_ld != out_ld)
+    return fail(V41_EINVAL, "%s: in place needs in_ld == out_ld", who);
+  return V41_OK;
+}
+
+}  // namespace
+
+int v41_rope_rows(const v41_bf16* in, int64_t in_ld, v41_bf16* out, int64_t out_ld,
+                  int32_t batch, int32_t n_tokens, int32_t rows_per_pos, int32_t row_len,
+                  int32_t rope_dim, const float* table, int64_t table_rows, const int32_t* pos,
+                  int64_t start_pos, int32_t inverse, v41_stream stream) {
+  const int64_t rows = (int64_t)batch * n_tokens * rows_per_pos;
+  if (rows > 0 && out == nullptr) return fail(V41_EINVAL, "rope_rows: NULL out");
+  int rc = check_rope_rows("rope_rows", in, in_ld, out, out_ld, batch, n_tokens, rows_per_pos,
+                           row_len, rope_dim, table, table_rows, pos, start_pos, 8);
+  if (rc) return rc;
+  rc = check_device();
+  if (rc) return rc;
+  v41::RopeRowsArgs a{in, in_ld, out, out_ld, batch, n_tokens, rows_per_pos, row_len,
+                      rope_dim, table, table_rows, pos, start_pos, inverse != 0, false,
+                      nullptr, 0, 0};
+  return launched(v41::launch_rope_rows(a, (hipStream_t)stream), "rope_rows");
+}
+
+int v41_rope_fp8_rows(const v41_bf16* in, int64_t in_ld, v41_bf16* out, int64_t out_ld,
+                      int32_t batch, int32_t n_tokens, int32_t row_len, int32_t rope_dim,
+                      const float* table, int64_t table_rows, const int32_t* pos,
+                      int64_t start_pos, v41_bf16* ring, int32_t ring_slots, int64_t ring_bs,
+                      v41_stream stream) {
+  const int64_t rows = (int64_t)batch * n_tokens;
+  if (rows > 0 && out == nullptr && ring == nullptr)
+    return fail(V41_EINVAL, "rope_fp8_rows: neither out nor ring given");
+  int rc = check_rope_rows("rope_fp8_rows", in, in_ld, out, out_ld, batch, n_tokens, 1,
+                           row_len, rope_dim, table, table_rows, pos, start_pos,
+                           V41_FP8_BLOCK);
+  if (rc) return rc;
+  if (!aligned16(ring)) return fail(V41_EINVAL, "rope_fp8_rows: ring must be 16-byte aligned");
+  if (ring != nullptr) {
+    if (ring_slots <= 0) return fail(V41_EINVAL, "rope_fp8_rows: ring given with ring_slots <= 0");
+    if (batch > 1 && ring_bs < (int64_t)ring_slots * row_len)
+      return fail(V41_EINVAL, "rope_fp8_rows: ring_bs smaller than ring_slots * row_len");
+    const char* r0 = reinterpret_cast<const char*>(ring);
+    const char* i0 = reinterpret_cast<const char*>(in);
+    const int64_t span_ring =
+        ((batch > 1 ? (int64_t)(batch - 1) * ring_bs : 0) + (int64_t)ring_slots * row_len) * 2;
+    const int64_t span_in = rows > 0 ? ((rows - 1) * in_ld + row_len) * 2 : 0;
+    if (rows > 0 && i0 < r0 + span_ring && r0 < i0 + span_in)
+      return fail(V41_EINVAL, "rope_fp8_rows: in overlaps the ring");
+  }
+  rc = check_device();
+  if (rc) return rc;
+  v41::RopeRowsArgs a{in, in_ld, out, out_ld, batch, n_tokens, 1, row_len, rope_dim,
+                      table, table_rows, pos, start_pos, false, true, ring,
+                      ring != nullptr ? ring_slots : 0, ring_bs};
+  return launched(v41::launch_rope_rows(a, (hipStream_t)stream), "rope_fp8_rows");
 }
 
 }  // extern "C"

@@ -17,6 +17,11 @@ The window rows are the chunk at position 0 and the ring otherwise (the
 columns, offset by the window row count (the join J = [J^w ; I + |W|] of the
 "Compressed sparse attention" page).
 
+With a RopeTable (the rotary epilogue before the path), q arrives before its
+rotation and is rotated in place, and step 1 becomes the fused rotation + fp8
+round trip + ring write of the new kv rows (W_{t,448:} <- R_t w; W <- FP8(W)).
+At decode the positions are read on the device from an int32 [B] tensor.
+
 Buffers are torch tensors owned by the caller (bf16 data as torch.bfloat16,
 f32, int32, uint8).  Nothing here computes: every step is a libv41 call.
 """
@@ -52,6 +57,23 @@ class Geometry:
     topk: int
     ratio: int
     scale: float
+
+
+@dataclass
+class RopeTable:
+    """The ratio-0 RoPE table on the device: f32 [n_pos, rope_dim / 2, 2]."""
+    table: torch.Tensor
+    rope_dim: int
+
+    @property
+    def n_pos(self) -> int:
+        return self.table.shape[0]
+
+
+def rope_table(theta: float, rope_dim: int, n_pos: int, device, stream=None) -> RopeTable:
+    t = torch.empty(n_pos, rope_dim // 2, 2, dtype=torch.float32, device=device)
+    v41.v41_rope_table(theta, rope_dim, n_pos, t, stream=stream)
+    return RopeTable(table=t, rope_dim=rope_dim)
 
 
 @dataclass
@@ -101,14 +123,25 @@ def alloc_decode(geo: Geometry, batch: int, n_rows: int, device) -> DecodeBuffer
         workspace=ws)
 
 
-def decode_step(buf: DecodeBuffers, pos: int, stream=None) -> None:
+def decode_step(buf: DecodeBuffers, pos: int, stream=None, rope: RopeTable | None = None,
+                pos_dev: torch.Tensor | None = None) -> None:
+    """One decode step at position pos (the same for every sequence); with
+    rope, q is rotated in place and pos_dev (int32 [B], optional) gives each
+    sequence's position on the device for the rotations and the ring slot."""
     g = buf.geo
     B, D, W, L = buf.batch, g.head_dim, g.window, buf.n_rows
     width = buf.width
     slot = pos % W
-    # 1. fp8 round trip of the new rows into their ring slots
-    v41.v41_fp8_round_rows(buf.kv_new, D, buf.ring.data_ptr() + 2 * slot * D, W * D, B, D,
-                           stream=stream)
+    if rope is not None:
+        # 0. rotate q; 1. rotate + fp8 the new rows straight into their slots
+        v41.v41_rope_rows(buf.q, D, buf.q, D, B, 1, g.n_heads, D, rope.rope_dim, rope.table,
+                          rope.n_pos, pos_dev, pos, 0, stream=stream)
+        v41.v41_rope_fp8_rows(buf.kv_new, D, None, D, B, 1, D, rope.rope_dim, rope.table,
+                              rope.n_pos, pos_dev, pos, buf.ring, W, W * D, stream=stream)
+    else:
+        # 1. fp8 round trip of the new rows into their ring slots
+        v41.v41_fp8_round_rows(buf.kv_new, D, buf.ring.data_ptr() + 2 * slot * D, W * D, B, D,
+                               stream=stream)
     # 2. the ring, oldest first
     v41.v41_window_idx(pos, 1, W, B, buf.idx, width, width, stream=stream)
     if g.ratio > 0:
@@ -179,12 +212,20 @@ def alloc_prefill(geo: Geometry, n_tokens: int, n_rows: int, cand_width: int, ca
         out=torch.zeros(T, geo.n_heads, D, dtype=BF16, **e))
 
 
-def prefill_chunk(buf: PrefillBuffers, stream=None) -> None:
+def prefill_chunk(buf: PrefillBuffers, stream=None, rope: RopeTable | None = None) -> None:
     g = buf.geo
     T, D, W, L = buf.n_tokens, g.head_dim, g.window, buf.n_rows
     width, cols = buf.width, buf.cols
-    # 1. fp8 round trip of the chunk's rows, seeding the ring with the last W
-    v41.v41_fp8_round_rows(buf.kv_chunk, D, buf.rows_a, D, T, D, buf.ring, W, 0, stream=stream)
+    if rope is not None:
+        # 0. rotate q; 1. rotate + fp8 the chunk's rows, seeding the ring
+        v41.v41_rope_rows(buf.q, D, buf.q, D, 1, T, g.n_heads, D, rope.rope_dim, rope.table,
+                          rope.n_pos, None, 0, 0, stream=stream)
+        v41.v41_rope_fp8_rows(buf.kv_chunk, D, buf.rows_a, D, 1, T, D, rope.rope_dim,
+                              rope.table, rope.n_pos, None, 0, buf.ring, W, 0, stream=stream)
+    else:
+        # 1. fp8 round trip of the chunk's rows, seeding the ring with the last W
+        v41.v41_fp8_round_rows(buf.kv_chunk, D, buf.rows_a, D, T, D, buf.ring, W, 0,
+                               stream=stream)
     # 2. causal window into the chunk
     v41.v41_window_idx(0, T, W, 1, buf.idx, width, T * width, stream=stream)
     if g.ratio > 0:

@@ -17,7 +17,8 @@ LIB_PATH = os.path.join(_HERE, "libv41.so")
 V41_OK, V41_EINVAL, V41_EHIP, V41_EDEVICE = 0, -1, -2, -3
 EXPORTS = ("v41_last_error", "v41_abi_version", "v41_fp8_round_rows", "v41_window_idx",
            "v41_indexer_scores", "v41_topk_select", "v41_sparse_attn_sink",
-           "v41_sparse_attn_workspace_bytes")
+           "v41_sparse_attn_workspace_bytes", "v41_rope_table", "v41_rope_rows",
+           "v41_rope_fp8_rows")
 
 
 class V41Error(RuntimeError):
@@ -57,6 +58,14 @@ def load() -> C.CDLL:
                                        i32, i32, i32, i32, vp, vp, i64, vp]
     L.v41_sparse_attn_workspace_bytes.restype = C.c_int64
     L.v41_sparse_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.v41_rope_table.restype = C.c_int
+    L.v41_rope_table.argtypes = [C.c_double, i32, i64, vp, vp]
+    L.v41_rope_rows.restype = C.c_int
+    L.v41_rope_rows.argtypes = [vp, i64, vp, i64, i32, i32, i32, i32, i32, vp, i64, vp, i64,
+                                i32, vp]
+    L.v41_rope_fp8_rows.restype = C.c_int
+    L.v41_rope_fp8_rows.argtypes = [vp, i64, vp, i64, i32, i32, i32, i32, vp, i64, vp, i64,
+                                    vp, i32, i64, vp]
     _lib = L
     return L
 
@@ -134,3 +143,23 @@ def v41_sparse_attn_sink(q, rows_a, rows_a_len, a_bs, rows_b, rows_b_len, b_bs, 
 def v41_sparse_attn_workspace_bytes(batch, n_tokens, n_heads, head_dim, width) -> int:
     return int(load().v41_sparse_attn_workspace_bytes(batch, n_tokens, n_heads, head_dim,
                                                       width))
+
+
+def v41_rope_table(theta, rope_dim, n_pos, table, stream=None) -> None:
+    _check(load().v41_rope_table(float(theta), rope_dim, n_pos, _ptr(table), _stream(stream)))
+
+
+def v41_rope_rows(inp, in_ld, out, out_ld, batch, n_tokens, rows_per_pos, row_len, rope_dim,
+                  table, table_rows, pos=None, start_pos=0, inverse=0, stream=None) -> None:
+    _check(load().v41_rope_rows(_ptr(inp), in_ld, _ptr(out), out_ld, batch, n_tokens,
+                                rows_per_pos, row_len, rope_dim, _ptr(table), table_rows,
+                                _ptr(pos), start_pos, int(inverse), _stream(stream)))
+
+
+def v41_rope_fp8_rows(inp, in_ld, out, out_ld, batch, n_tokens, row_len, rope_dim, table,
+                      table_rows, pos=None, start_pos=0, ring=None, ring_slots=0, ring_bs=0,
+                      stream=None) -> None:
+    _check(load().v41_rope_fp8_rows(_ptr(inp), in_ld, _ptr(out), out_ld, batch, n_tokens,
+                                    row_len, rope_dim, _ptr(table), table_rows, _ptr(pos),
+                                    start_pos, _ptr(ring), ring_slots, ring_bs,
+                                    _stream(stream)))

@@ -14,7 +14,8 @@ Five workloads, named for what they are:
 
 Layer geometry of the large workloads: 64 heads x 512, window 128, indexer 64
 heads x 128, top-512, ratio 4, sink N(0,1), softmax scale 1/sqrt(512) held as
-binary32.  Seeds: 0x5EED0000 + 1000 * workload_id + sequence.
+binary32; RoPE on the last 64 values of each q and kv row with base 10000 (the
+last 16 in the tiny pair) when the rotary epilogue is part of the step.  Seeds: 0x5EED0000 + 1000 * workload_id + sequence.
 
 Every array is raw: bf16 values as uint16 bits, f32 as float32.  The kv rows
 that the method rounds through fp8 come out unrounded here; whoever consumes
@@ -54,6 +55,8 @@ class Workload:
     cand_block: int = 0  # 0 = no candidate mask
     cand_width: int = 0
     ties: bool = False
+    rope_dim: int = 64            # rotated tail of each q / kv row (rope_head_dim)
+    rope_theta: float = 10000.0   # ratio-0 table base (rope_theta)
 
     def seed(self, seq: int) -> int:
         return SEED_BASE + 1000 * self.wid + seq
@@ -97,7 +100,7 @@ WORKLOADS = {
 # The tiny pair: layer 0 has ratio 0 (window only), layer 1 ratio 4.
 TINY = Workload(0, "tiny", "tiny", batch=1, n_tokens=12, start_pos=0,
                 n_heads=4, head_dim=64, window=8, index_heads=2, index_dim=32,
-                topk=2, ratio=4, n_rows=4, w_scale=1.0)
+                topk=2, ratio=4, n_rows=4, w_scale=1.0, rope_dim=16)
 TINY_DECODE_POSITIONS = (12, 13)
 
 

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib.v41_abi_version() == 1
+    assert lib.v41_abi_version() == 2
 
 
 def _err(lib):
@@ -105,3 +105,42 @@ def test_workspace_query(lib):
     assert lib.v41_sparse_attn_workspace_bytes(64, 1, 64, 512, 640) == 0
     # many queries: no split
     assert lib.v41_sparse_attn_workspace_bytes(1, 2048, 64, 512, 640) == 0
+
+
+def test_rope_table_rejects_odd_dim_and_theta(lib):
+    assert lib.v41_rope_table(10000.0, 63, 4, 1024, None) == -1 and "even" in _err(lib)
+    assert lib.v41_rope_table(0.0, 64, 4, 1024, None) == -1 and "theta" in _err(lib)
+    assert lib.v41_rope_table(10000.0, 64, 4, 1028, None) == -1 and "aligned" in _err(lib)
+
+
+def test_rope_rows_rejects_bad_shapes(lib):
+    # rope_dim not a multiple of 8
+    assert lib.v41_rope_rows(1024, 64, 1024, 64, 1, 1, 1, 64, 12, 4096, 10, None, 0, 0,
+                             None) == -1 and "rope_dim" in _err(lib)
+    # rope_dim wider than the row
+    assert lib.v41_rope_rows(1024, 64, 1024, 64, 1, 1, 1, 64, 72, 4096, 10, None, 0, 0,
+                             None) == -1
+    # host positions past the table
+    assert lib.v41_rope_rows(1024, 64, 1024, 64, 1, 4, 1, 64, 16, 4096, 10, None, 7, 0,
+                             None) == -1 and "outside the table" in _err(lib)
+    # distinct but overlapping in and out
+    assert lib.v41_rope_rows(1 << 20, 64, (1 << 20) + 16, 64, 1, 4, 1, 64, 16, 4096, 10, None,
+                             0, 0, None) == -1 and "overlap" in _err(lib)
+    # in place with different strides
+    assert lib.v41_rope_rows(1 << 20, 64, 1 << 20, 72, 1, 4, 1, 64, 16, 4096, 10, None, 0, 0,
+                             None) == -1
+
+
+def test_rope_fp8_rows_rejects_bad_shapes(lib):
+    # row_len not a multiple of the fp8 block
+    assert lib.v41_rope_fp8_rows(1024, 48, 4096, 48, 1, 1, 48, 16, 8192, 10, None, 0, None, 0,
+                                 0, None) == -1 and "row_len" in _err(lib)
+    # nowhere to write
+    assert lib.v41_rope_fp8_rows(1024, 64, None, 64, 1, 1, 64, 16, 8192, 10, None, 0, None, 0,
+                                 0, None) == -1 and "neither" in _err(lib)
+    # ring too small for the batch stride
+    assert lib.v41_rope_fp8_rows(1 << 20, 64, None, 64, 2, 1, 64, 16, 8192, 10, None, 0,
+                                 1 << 24, 8, 64, None) == -1 and "ring_bs" in _err(lib)
+    # ring overlapping the input rows
+    assert lib.v41_rope_fp8_rows(1 << 20, 64, None, 64, 1, 4, 64, 16, 8192, 10, None, 0,
+                                 (1 << 20) + 256, 8, 512, None) == -1 and "overlaps" in _err(lib)

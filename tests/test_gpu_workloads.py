@@ -167,3 +167,118 @@ def test_tiny_pair_chain():
         assert np.array_equal(LY.to_numpy_bf16(dec.ring[0]), ring.rows)
         assert np.array_equal(dec.idx.cpu().numpy(), want["idx"])
         assert_attn_close(LY.to_numpy_bf16(dec.out), want["out"], f"tiny ratio-0 decode {p}")
+
+
+# ------------------------------------------------------------------ with the rotary epilogue
+def oracle_table_at(buf, wl, positions):
+    """The oracle's RoPE table, after checking that the GPU's table rows at
+    `positions` are bit-identical to it (then every rotation and fp8 decision
+    below is taken on the same numbers on both sides)."""
+    gpu = buf.rope.table.cpu().numpy()
+    ora = O.rope_table(wl.rope_theta, wl.rope_dim, gpu.shape[0])
+    for p in positions:
+        assert np.array_equal(gpu[p], ora[p]), f"table row {p} differs from the oracle's"
+    return ora
+
+
+def test_decode64_rope_sampled():
+    wl = W.WORKLOADS["decode64"]
+    say("decode64 + rope staging")
+    buf, host = bench.stage_decode(wl, DEV, keep_host=True)
+    buf.pos = wl.start_pos
+    bench.attach_rope(buf, wl, DEV)
+    for _, f in bench.step_calls(buf, "decode", rope=True):
+        f()
+    torch.cuda.synchronize()
+    p, W_, H, rd = wl.start_pos, wl.window, wl.n_heads, wl.rope_dim
+    tab = oracle_table_at(buf, wl, [p])
+    sink = W.layer_sink(wl)
+    q = LY.to_numpy_bf16(buf.q)
+    ring = LY.to_numpy_bf16(buf.ring)
+    idx = buf.idx.cpu().numpy()
+    out = LY.to_numpy_bf16(buf.out)
+    slot = p % W_
+    q_host = np.stack([host[b]["q"][0] for b in range(wl.batch)])
+    want_q = O.rope_rows(q_host, tab, np.full(wl.batch * H, p), rd).reshape(q_host.shape)
+    assert np.array_equal(q, want_q), "rotated q"
+    for b in range(wl.batch):
+        want_ring = O.fp8_round_rows(host[b]["ring_raw"])
+        want_ring[slot] = O.rope_fp8_rows(host[b]["kv_new"], tab, [p], rd)[0]
+        assert np.array_equal(ring[b], want_ring), f"ring of sequence {b}"
+    assert np.array_equal(idx[:, W_:], O.topk(buf.scores.cpu().numpy(), wl.topk, W_)), "top-k"
+    for b in (0, 31, 63):
+        say("decode64 + rope attention", b)
+        ora_o = O.sparse_attn(want_q[b:b + 1], ring[b], host[b]["latent"], idx[b:b + 1], sink,
+                              wl.scale)
+        assert_attn_close(out[b:b + 1], ora_o, f"decode64 + rope attention b={b}")
+
+
+def test_prefill_rope_sampled():
+    wl = W.WORKLOADS["prefill"]
+    say("prefill + rope staging")
+    buf, d = bench.stage_prefill(wl, DEV, keep_host=True)
+    bench.attach_rope(buf, wl, DEV)
+    for _, f in bench.step_calls(buf, "prefill", rope=True):
+        f()
+    torch.cuda.synchronize()
+    T, W_, H, rd = wl.n_tokens, wl.window, wl.n_heads, wl.rope_dim
+    tab = oracle_table_at(buf, wl, range(T))
+    want_q = O.rope_rows(d["q"], tab, np.repeat(np.arange(T), H), rd).reshape(d["q"].shape)
+    assert np.array_equal(LY.to_numpy_bf16(buf.q), want_q), "rotated q"
+    want_rows = O.rope_fp8_rows(d["kv_chunk"], tab, np.arange(T), rd)
+    rows_a = LY.to_numpy_bf16(buf.rows_a)
+    assert np.array_equal(rows_a, want_rows), "rotated fp8 rows"
+    ring = O.WindowCache(W_, wl.head_dim)
+    ring.prefill(want_rows)
+    assert np.array_equal(LY.to_numpy_bf16(buf.ring), ring.rows), "ring"
+    idx = buf.idx.cpu().numpy()
+    toks = [0, 1, 127, 128, 1500, 2047]
+    say("prefill + rope tokens", toks)
+    out = LY.to_numpy_bf16(buf.out)
+    ora_o = O.sparse_attn(want_q[toks], rows_a, d["latent"], idx[toks], W.layer_sink(wl),
+                          wl.scale)
+    assert_attn_close(out[toks], ora_o, "prefill + rope attention")
+
+
+def test_tiny_ratio0_chain_with_rope():
+    """The ratio-0 layer of the tiny pair with the rotary epilogue (RoPE on
+    the last 16 values): prefill of 12 tokens, then decodes 12 and 13 through
+    one ring, device positions at decode."""
+    wl = W.TINY
+    d = W.tiny_inputs(0)
+    geo = LY.Geometry(n_heads=wl.n_heads, head_dim=wl.head_dim, window=wl.window,
+                      index_heads=wl.index_heads, index_dim=wl.index_dim, topk=wl.topk,
+                      ratio=0, scale=wl.scale)
+    T, D, W_ = wl.n_tokens, wl.head_dim, wl.window
+    say("tiny ratio-0 + rope")
+    rt = LY.rope_table(wl.rope_theta, wl.rope_dim, 14, DEV)
+    tab = O.rope_table(wl.rope_theta, wl.rope_dim, 14)
+    assert np.array_equal(rt.table.cpu().numpy(), tab)
+    pre = LY.alloc_prefill(geo, T, 0, 0, 1, DEV)
+    pre.kv_chunk.copy_(LY.to_device_bf16(d["kv_chunk"], DEV))
+    pre.q.copy_(LY.to_device_bf16(d["q"], DEV))
+    pre.sink.copy_(torch.from_numpy(d["sink"]).to(DEV))
+    LY.prefill_chunk(pre, rope=rt)
+    torch.cuda.synchronize()
+    ring = O.WindowCache(W_, D)
+    want = OL.prefill(d["kv_chunk"], d["q"], d["sink"], wl.scale, W_, ring=ring,
+                      rope=(tab, wl.rope_dim))
+    assert np.array_equal(LY.to_numpy_bf16(pre.q), want["q"])
+    assert np.array_equal(LY.to_numpy_bf16(pre.rows_a), want["rows_a"])
+    assert np.array_equal(LY.to_numpy_bf16(pre.ring), ring.rows)
+    assert_attn_close(LY.to_numpy_bf16(pre.out), want["out"], "tiny ratio-0 + rope prefill")
+    dec = LY.alloc_decode(geo, 1, 0, DEV)
+    dec.ring[0].copy_(pre.ring)
+    dec.sink.copy_(pre.sink)
+    pos_dev = torch.zeros(1, dtype=torch.int32, device=DEV)
+    for p in W.TINY_DECODE_POSITIONS:
+        dec.kv_new[0].copy_(LY.to_device_bf16(d[f"kv_new_{p}"][0], DEV))
+        dec.q[0].copy_(LY.to_device_bf16(d[f"q_{p}"][0], DEV))
+        pos_dev.fill_(p)
+        LY.decode_step(dec, p, rope=rt, pos_dev=pos_dev)
+        torch.cuda.synchronize()
+        want = OL.decode(ring, d[f"kv_new_{p}"], p, d[f"q_{p}"], d["sink"], wl.scale,
+                         rope=(tab, wl.rope_dim))
+        assert np.array_equal(LY.to_numpy_bf16(dec.q), want["q"])
+        assert np.array_equal(LY.to_numpy_bf16(dec.ring[0]), ring.rows)
+        assert_attn_close(LY.to_numpy_bf16(dec.out), want["out"], f"tiny + rope decode {p}")
