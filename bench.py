@@ -8,10 +8,12 @@ batched decode: 64 sequences at context 32768 (8192 compressed rows each),
 token per sequence.  The prefill chunk (2048 tokens at position 0) is
 reported alongside.
 
-Input staging rotates several copies of every input tensor, so a step never
-reads what the previous step left in the 256 MB last-level cache (as in a
-model, where the other layers run in between).  Each step is captured once in
-a HIP graph per copy and replayed; per-kernel durations come from HIP events
+A decode step is one v41_decode_step call (four launches, positions read on
+the device); the same step as the five separate calls is timed alongside
+(--separate-calls makes that form the headline).  Input staging rotates several
+copies of every input tensor, so a step never reads what the previous step left
+in the 256 MB last-level cache (as in a model, where the other layers run in
+between).  Each step is captured once in a HIP graph per copy and replayed; per-kernel durations come from HIP events
 around graph replays of single kernels on the same stream.  The CPU baseline
 is the oracle (plain C, one thread) on a bounded sample of the same workload.
 
@@ -302,26 +304,13 @@ def cpu_baseline(wl, n_sample, budget_s=30.0):
 
 
 # ----------------------------------------------------------------- main
-def run_workload(name, steps, warmup, n_sets, torch, device, rope=False):
-    wl = WL.WORKLOADS[name]
-    t0 = time.time()
-    if wl.mode == "decode":
-        buf0, _ = stage_decode(wl, device)
-        buf0.pos = wl.start_pos
-    else:
-        buf0, _ = stage_prefill(wl, device)
-    if rope:
-        attach_rope(buf0, wl, device)
-    sets = [buf0] + [clone_buffers(buf0) for _ in range(n_sets - 1)]
-    for s in sets:
-        s.pos = getattr(buf0, "pos", 0)
-    log(f"{name}: staged {n_sets} input sets in {time.time() - t0:.1f}s")
-
-    calls = [step_calls(s, wl.mode, rope) for s in sets]
-    # One graph holds one step per input set, as one graph would hold the
-    # layers of a model; single-step graphs cover a remainder of K.
-    all_graph = capture([f for c in calls for _, f in c], torch)
-    one_graphs = [capture([f for _, f in c], torch) for c in calls]
+def timed_steps(step_fns, steps, warmup, torch):
+    """Mean ms per step: one graph holds one step per input set (as one graph
+    would hold the layers of a model), single-step graphs cover a remainder
+    of K; W warm-up steps first."""
+    n_sets = len(step_fns)
+    all_graph = capture([f for c in step_fns for f in c], torch)
+    one_graphs = [capture(c, torch) for c in step_fns]
     for i in range(max(1, warmup // n_sets)):
         all_graph.replay()
     torch.cuda.synchronize()
@@ -336,8 +325,49 @@ def run_workload(name, steps, warmup, n_sets, torch, device, rope=False):
         one_graphs[i].replay()
     e1.record(st)
     e1.synchronize()
-    ms_step = e0.elapsed_time(e1) / steps
-    log(f"{name}{' + rope' if rope else ''}: {ms_step * 1e3:.1f} us per step")
+    return e0.elapsed_time(e1) / steps, one_graphs
+
+
+def fused_call(buf, rope):
+    """The whole decode step as one v41_decode_step call (device positions)."""
+    from indexer_top_sink_amd import layer as LY
+    from indexer_top_sink_amd import v41
+    args = LY.decode_step_args(buf, buf.pos_dev, buf.rope if rope else None)
+    return lambda: v41.v41_decode_step(args)
+
+
+def run_workload(name, steps, warmup, n_sets, torch, device, rope=False, separate=False):
+    """Times K steps of a workload.  A decode step is one v41_decode_step call
+    (unless separate); its separate-call form is timed alongside.  Returns
+    (workload, ms per step, per-kernel us, algorithmic work, ms per step of
+    the separate calls or None)."""
+    wl = WL.WORKLOADS[name]
+    t0 = time.time()
+    if wl.mode == "decode":
+        buf0, _ = stage_decode(wl, device)
+        buf0.pos = wl.start_pos
+        buf0.pos_dev = torch.full((wl.batch,), wl.start_pos, dtype=torch.int32, device=device)
+    else:
+        buf0, _ = stage_prefill(wl, device)
+    if rope:
+        attach_rope(buf0, wl, device)
+    sets = [buf0] + [clone_buffers(buf0) for _ in range(n_sets - 1)]
+    for s in sets:
+        s.pos = getattr(buf0, "pos", 0)
+    log(f"{name}: staged {n_sets} input sets in {time.time() - t0:.1f}s")
+
+    calls = [step_calls(s, wl.mode, rope) for s in sets]
+    sep_fns = [[f for _, f in c] for c in calls]
+    ms_sep = None
+    if wl.mode == "decode" and not separate:
+        ms_step, one_graphs = timed_steps([[fused_call(s, rope)] for s in sets], steps, warmup,
+                                          torch)
+        ms_sep, _ = timed_steps(sep_fns, steps, warmup, torch)
+        log(f"{name}{' + rope' if rope else ''}: {ms_step * 1e3:.1f} us per step "
+            f"({ms_sep * 1e3:.1f} us as separate calls)")
+    else:
+        ms_step, one_graphs = timed_steps(sep_fns, steps, warmup, torch)
+        log(f"{name}{' + rope' if rope else ''}: {ms_step * 1e3:.1f} us per step")
 
     # per-kernel durations: a graph of 4 * n_sets launches of one kernel
     # cycling over the input sets, replayed; mean time per launch
@@ -362,7 +392,7 @@ def run_workload(name, steps, warmup, n_sets, torch, device, rope=False):
             blocks = np.repeat(cand[t].astype(bool), wl.cand_block)[:n]
             pairs += int(blocks.sum())
     work = algorithmic(wl, host_idx=idx, valid_pairs=pairs, rope=rope)
-    return wl, ms_step, kern_us, work
+    return wl, ms_step, kern_us, work, ms_sep
 
 
 # Sources of each kernel: a stored traffic figure holds only while they are
@@ -424,6 +454,9 @@ def main():
     ap.add_argument("--rope", action="store_true",
                     help="make the rotary epilogue (q rotation; kv rotation + fp8 + ring "
                          "write) part of the timed step")
+    ap.add_argument("--separate-calls", action="store_true",
+                    help="time a decode step as the separate calls instead of one "
+                         "v41_decode_step call")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0)
@@ -452,8 +485,10 @@ def main():
         log(f"copy calibration: {n} bytes read and {n} written per copy")
         del src, dst
 
-    wl, ms_step, kern_us, work = run_workload(args.workload, args.steps, args.warmup,
-                                              args.input_sets, torch, device, rope=args.rope)
+    wl, ms_step, kern_us, work, ms_sep = run_workload(args.workload, args.steps, args.warmup,
+                                                      args.input_sets, torch, device,
+                                                      rope=args.rope,
+                                                      separate=args.separate_calls)
     tokens = wl.queries
     value = tokens / (ms_step * 1e-3)
     # the dominant kernel is the one that takes the most time; decode moves
@@ -476,15 +511,18 @@ def main():
                    "head_dim": wl.head_dim, "window": wl.window,
                    "index_heads": wl.index_heads, "index_dim": wl.index_dim,
                    "topk": wl.topk, "ratio": wl.ratio, "hip_graph": True,
-                   "input_sets": args.input_sets, "rope_epilogue": bool(args.rope)},
+                   "input_sets": args.input_sets, "rope_epilogue": bool(args.rope),
+                   "step_form": ("separate calls" if args.separate_calls or wl.mode != "decode"
+                                 else "v41_decode_step")},
         "roofline": roof,
         "roofline_other": others,
         "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "ms_per_step_separate_calls": round(ms_sep, 5) if ms_sep is not None else None,
         "kernels_us": {k: round(v, 2) for k, v in kern_us.items()},
     }
     if not args.no_secondary and wl.name != "prefill":
-        pw, pms, pk, pwork = run_workload("prefill", max(12, args.steps // 2), 3,
-                                          args.input_sets, torch, device)
+        pw, pms, pk, pwork, _ = run_workload("prefill", max(12, args.steps // 2), 3,
+                                             args.input_sets, torch, device)
         out["secondary"] = {
             "prefill": {
                 "value": round(pw.n_tokens / (pms * 1e-3), 1), "unit": "tokens/s",
@@ -496,11 +534,13 @@ def main():
                 "kernels_us": {k: round(v, 2) for k, v in pk.items()}}}
     if not args.no_secondary and not args.rope:
         # the same step with the rotary epilogue in front (pre-rotation q and kv)
-        rw, rms, rk, rwork = run_workload(wl.name, args.steps, args.warmup, args.input_sets,
-                                          torch, device, rope=True)
+        rw, rms, rk, rwork, rsep = run_workload(wl.name, args.steps, args.warmup,
+                                                args.input_sets, torch, device, rope=True,
+                                                separate=args.separate_calls)
         out.setdefault("secondary", {})["with_rope_epilogue"] = {
             "value": round(rw.queries / (rms * 1e-3), 1), "unit": "tokens/s",
             "ms_per_step": round(rms, 5),
+            "ms_per_step_separate_calls": round(rsep, 5) if rsep is not None else None,
             "rope_rows": roofline_entry("rope_rows", rwork, rk["rope_rows"], "hbm", rw.name),
             "rope_fp8_rows": roofline_entry("rope_fp8_rows", rwork, rk["rope_fp8_rows"], "hbm",
                                             rw.name),

@@ -275,6 +275,81 @@ int v41_rope_fp8_rows(const v41_bf16 *in, int64_t in_ld, v41_bf16 *out, int64_t 
                       int64_t start_pos, v41_bf16 *ring, int32_t ring_slots,
                       int64_t ring_bs, v41_stream stream);
 
+/*
+ * One whole decode step in one call, with every position read on the device,
+ * so that a HIP graph captured once replays it at every later step (the
+ * captured decode step of "attn_v41.rs": the graph's ring_put reads pos[0]
+ * mod window on the device, and the per-step index buffers are rebuilt on the
+ * device instead of being uploaded).  The step is the same computation as the
+ * separate calls, in fewer launches:
+ *   1. one launch: when rope_dim > 0, the q tails rotated in place
+ *      (v41_rope_rows) and the new kv rows rotated; the kv rows through the
+ *      fp8 round trip into ring slot pos[b] mod window (v41_fp8_round_rows /
+ *      v41_rope_fp8_rows); the window indices of the whole ring, oldest first
+ *      (v41_window_idx at a decode);
+ *   2. when ratio >= 1: the indexer scores with n(b) =
+ *      min(n_rows, floor((pos[b] + 1) / ratio)) (v41_indexer_scores), then
+ *      the top-k written after the window columns, offset by window
+ *      (v41_topk_select);
+ *   3. the sparse attention with the sink over [ring ; latent rows]
+ *      (v41_sparse_attn_sink).
+ * Sequences may sit at different positions.  A sequence whose pos[b] is
+ * negative, or (with rope) not below rope_rows, writes no ring row and has an
+ * empty window; its q is not rotated.
+ *
+ * Buffers (device, 16-byte aligned; contiguous unless a stride is given):
+ *   pos      int32 [batch]
+ *   q        bf16 [batch][n_heads][head_dim] (before the rotation when
+ *            rope_dim > 0; rotated in place)
+ *   kv_new   bf16 [batch][head_dim]
+ *   ring     bf16 [batch] x [window][head_dim] at ring + b * ring_bs
+ *   latent   bf16 [batch] x [n_rows][head_dim] at latent + b * latent_bs
+ *   kI       bf16 [batch] x [n_rows][index_dim] at kI + b * kI_bs
+ *   qI, w    bf16 [batch][index_heads][index_dim], f32 [batch][index_heads]
+ *   rope_table f32 [rope_rows][rope_dim / 2][2] (NULL iff rope_dim == 0)
+ *   sink     f32 [n_heads]
+ *   scores   f32 [batch][n_rows] (ratio >= 1)
+ *   idx      int32 [batch][window + topk] (topk counted only at ratio >= 1)
+ *   out      bf16 [batch][n_heads][head_dim]
+ *   workspace as for v41_sparse_attn_sink with width = window + topk.
+ * Geometry limits are those of the separate calls.  Calls sharing buffers
+ * must not overlap in time.
+ */
+typedef struct v41_decode_step_args {
+  int32_t batch;
+  int32_t n_heads;
+  int32_t head_dim;
+  int32_t window;
+  int32_t ratio;
+  int32_t index_heads;
+  int32_t index_dim;
+  int32_t topk;
+  int32_t rope_dim;
+  float scale;
+  int64_t n_rows;
+  int64_t rope_rows;
+  int64_t ring_bs;
+  int64_t latent_bs;
+  int64_t kI_bs;
+  int64_t workspace_bytes;
+  const int32_t *pos;
+  v41_bf16 *q;
+  const v41_bf16 *kv_new;
+  v41_bf16 *ring;
+  const v41_bf16 *latent;
+  const v41_bf16 *kI;
+  const v41_bf16 *qI;
+  const float *w;
+  const float *rope_table;
+  const float *sink;
+  float *scores;
+  int32_t *idx;
+  v41_bf16 *out;
+  void *workspace;
+} v41_decode_step_args;
+
+int v41_decode_step(const v41_decode_step_args *args, v41_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

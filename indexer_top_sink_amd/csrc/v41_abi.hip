@@ -63,7 +63,7 @@ extern "C" {
 
 const char* v41_last_error(void) { return g_err; }
 
-int v41_abi_version(void) { return 2; }
+int v41_abi_version(void) { return 3; }
 
 int v41_fp8_round_rows(const v41_bf16* in, int64_t in_ld, v41_bf16* out, int64_t out_ld,
                        int64_t rows, int32_t row_len, v41_bf16* ring, int32_t ring_slots,
@@ -148,8 +148,8 @@ int v41_indexer_scores(const v41_bf16* qI, const v41_bf16* kI, int64_t kI_bs, co
   int rc = check_device();
   if (rc) return rc;
   return launched(v41::launch_indexer_scores(qI, kI, kI_bs, w, cand, cand_width, cand_block,
-                                             batch, n_tokens, start_pos, ratio, n_heads,
-                                             head_dim, n_rows, scores, scores_ld,
+                                             batch, n_tokens, start_pos, nullptr, ratio,
+                                             n_heads, head_dim, n_rows, scores, scores_ld,
                                              (hipStream_t)stream),
                   "indexer_scores");
 }
@@ -353,6 +353,124 @@ int v41_rope_fp8_rows(const v41_bf16* in, int64_t in_ld, v41_bf16* out, int64_t 
                       table, table_rows, pos, start_pos, false, true, ring,
                       ring != nullptr ? ring_slots : 0, ring_bs};
   return launched(v41::launch_rope_rows(a, (hipStream_t)stream), "rope_fp8_rows");
+}
+
+int v41_decode_step(const v41_decode_step_args* a, v41_stream stream) {
+  const char* who = "decode_step";
+  if (a == nullptr) return fail(V41_EINVAL, "%s: NULL args", who);
+  if (a->batch < 0) return fail(V41_EINVAL, "%s: batch < 0", who);
+  if (a->n_heads < 1) return fail(V41_EINVAL, "%s: n_heads < 1", who);
+  const int32_t D = a->head_dim;
+  if (D != 64 && D != 128 && D != 256 && D != 512)
+    return fail(V41_EINVAL, "%s: head_dim %d not in {64, 128, 256, 512}", who, D);
+  if (a->window < 1) return fail(V41_EINVAL, "%s: window < 1", who);
+  if (a->ratio < 0) return fail(V41_EINVAL, "%s: ratio < 0", who);
+  const bool compressed = a->ratio >= 1;
+  const int32_t topk = compressed ? a->topk : 0;
+  if (compressed) {
+    if (a->topk < 1) return fail(V41_EINVAL, "%s: topk < 1", who);
+    if (a->index_heads < 1 || a->index_heads > V41_MAX_INDEX_HEADS)
+      return fail(V41_EINVAL, "%s: index_heads %d outside 1..%d", who, a->index_heads,
+                  V41_MAX_INDEX_HEADS);
+    if (a->index_dim != 32 && a->index_dim != 64 && a->index_dim != 128)
+      return fail(V41_EINVAL, "%s: index_dim %d not in {32, 64, 128}", who, a->index_dim);
+    if (a->n_rows < 0 || a->n_rows >= 0x7FFFFFFFLL - a->window)
+      return fail(V41_EINVAL, "%s: n_rows out of range", who);
+  }
+  const int64_t width = (int64_t)a->window + topk;
+  if (width > V41_MAX_WIDTH)
+    return fail(V41_EINVAL, "%s: window + topk = %lld exceeds the selection limit %d", who,
+                (long long)width, V41_MAX_WIDTH);
+  if (a->rope_dim < 0 || a->rope_dim % 8 != 0 || a->rope_dim > D)
+    return fail(V41_EINVAL, "%s: rope_dim %d must be a multiple of 8 in 0..head_dim", who,
+                a->rope_dim);
+  if ((a->rope_dim > 0) != (a->rope_table != nullptr))
+    return fail(V41_EINVAL, "%s: rope_table must be given exactly when rope_dim > 0", who);
+  if (a->rope_dim > 0 && a->rope_rows < 1)
+    return fail(V41_EINVAL, "%s: rope_rows < 1", who);
+  if (a->batch > 1 && a->ring_bs < (int64_t)a->window * D)
+    return fail(V41_EINVAL, "%s: ring_bs < window * head_dim", who);
+  if (compressed && a->batch > 1 && a->n_rows > 0 &&
+      (a->latent_bs < a->n_rows * D || a->kI_bs < a->n_rows * a->index_dim))
+    return fail(V41_EINVAL, "%s: latent_bs/kI_bs smaller than one sequence's rows", who);
+  if (a->ring_bs % 8 != 0 || a->latent_bs % 8 != 0 || a->kI_bs % 8 != 0)
+    return fail(V41_EINVAL, "%s: ring_bs/latent_bs/kI_bs must be multiples of 8", who);
+  if ((int64_t)a->batch * a->n_heads * (D / 8) >= 0x7FFFFFFFLL)
+    return fail(V41_EINVAL, "%s: batch too large", who);
+  if (a->batch > 0) {
+    if (a->pos == nullptr || a->q == nullptr || a->kv_new == nullptr || a->ring == nullptr ||
+        a->sink == nullptr || a->idx == nullptr || a->out == nullptr)
+      return fail(V41_EINVAL, "%s: NULL pos/q/kv_new/ring/sink/idx/out", who);
+    if (compressed && a->n_rows > 0 &&
+        (a->latent == nullptr || a->kI == nullptr || a->qI == nullptr || a->w == nullptr ||
+         a->scores == nullptr))
+      return fail(V41_EINVAL, "%s: NULL latent/kI/qI/w/scores (no latent cache published)", who);
+  }
+  if (!aligned16(a->pos) || !aligned16(a->q) || !aligned16(a->kv_new) ||
+      !aligned16(a->ring) || !aligned16(a->latent) || !aligned16(a->kI) ||
+      !aligned16(a->qI) || !aligned16(a->rope_table) || !aligned16(a->out) ||
+      !aligned16(a->workspace))
+    return fail(V41_EINVAL, "%s: pointers must be 16-byte aligned", who);
+  if (a->workspace_bytes < 0) return fail(V41_EINVAL, "%s: workspace_bytes < 0", who);
+  int rc = check_device();
+  if (rc) return rc;
+  if (a->batch == 0) {
+    g_err[0] = '\0';
+    return V41_OK;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  v41::DecodeFrontArgs f;
+  f.q = a->q;
+  f.kv = a->kv_new;
+  f.ring = a->ring;
+  f.ring_bs = a->ring_bs;
+  f.idx = a->idx;
+  f.idx_ld = width;
+  f.pos = a->pos;
+  f.table = a->rope_table;
+  f.table_rows = a->rope_rows;
+  f.batch = a->batch;
+  f.n_heads = a->n_heads;
+  f.row_len = D;
+  f.window = a->window;
+  f.rope_dim = a->rope_dim;
+  rc = launched(v41::launch_decode_front(f, s), "decode_step front");
+  if (rc) return rc;
+  const int64_t n_rows = compressed ? a->n_rows : 0;
+  if (compressed) {
+    // start_pos 1 only marks the decode form; the positions come from pos
+    rc = launched(v41::launch_indexer_scores(a->qI, a->kI, a->kI_bs, a->w, nullptr, 0, 1,
+                                             a->batch, 1, 1, a->pos, a->ratio, a->index_heads,
+                                             a->index_dim, n_rows, a->scores, n_rows, s),
+                  "decode_step indexer");
+    if (rc) return rc;
+    // with no compressed rows the top-k reads nothing and writes k absent entries
+    rc = launched(v41::launch_topk_select(a->scores, a->batch, n_rows, n_rows, topk, a->window,
+                                          a->idx + a->window, width, s),
+                  "decode_step top-k");
+    if (rc) return rc;
+  }
+  v41::AttnArgs t;
+  t.q = a->q;
+  t.rows_a = a->ring;
+  t.rows_a_len = a->window;
+  t.a_bs = a->ring_bs;
+  t.rows_b = compressed && n_rows > 0 ? a->latent : nullptr;
+  t.rows_b_len = compressed ? n_rows : 0;
+  t.b_bs = a->latent_bs;
+  t.idx = a->idx;
+  t.width = (int32_t)width;
+  t.idx_ld = width;
+  t.sink = a->sink;
+  t.scale = a->scale;
+  t.batch = a->batch;
+  t.n_tokens = 1;
+  t.n_heads = a->n_heads;
+  t.head_dim = D;
+  t.out = a->out;
+  t.workspace = a->workspace;
+  t.workspace_bytes = a->workspace ? a->workspace_bytes : 0;
+  return launched(v41::launch_sparse_attn_sink(t, s), "decode_step attention");
 }
 
 }  // extern "C"

@@ -50,9 +50,9 @@ hipError_t launch_window_idx(int64_t start_pos, int32_t n_tokens, int32_t window
 hipError_t launch_indexer_scores(const uint16_t* qI, const uint16_t* kI, int64_t kI_bs,
                                  const float* w, const uint8_t* cand, int32_t cand_width,
                                  int32_t cand_block, int32_t batch, int32_t n_tokens,
-                                 int64_t start_pos, int32_t ratio, int32_t n_heads,
-                                 int32_t head_dim, int64_t n_rows, float* scores,
-                                 int64_t scores_ld, hipStream_t s);
+                                 int64_t start_pos, const int32_t* pos, int32_t ratio,
+                                 int32_t n_heads, int32_t head_dim, int64_t n_rows,
+                                 float* scores, int64_t scores_ld, hipStream_t s);
 
 hipError_t launch_topk_select(const float* scores, int64_t n_sel_rows, int64_t n_cols,
                               int64_t scores_ld, int32_t k, int32_t offset, int32_t* idx,

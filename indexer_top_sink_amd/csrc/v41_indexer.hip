@@ -113,8 +113,9 @@ template <int DI, int HT, int NT>
 __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(
     const uint16_t* __restrict__ qI, const uint16_t* __restrict__ kI, int64_t kI_bs,
     const float* __restrict__ w, const uint8_t* __restrict__ cand, int32_t cand_width,
-    int32_t cand_block, int32_t n_tokens, int64_t start_pos, int32_t ratio, int32_t n_heads,
-    int32_t n_rows, float* __restrict__ scores, int64_t scores_ld, int32_t blocks_per_query) {
+    int32_t cand_block, int32_t n_tokens, int64_t start_pos, const int32_t* __restrict__ pos,
+    int32_t ratio, int32_t n_heads, int32_t n_rows, float* __restrict__ scores,
+    int64_t scores_ld, int32_t blocks_per_query) {
   using KT = KeyTile<DI>;
   constexpr int KS = KT::KS;
   constexpr int kQBytes = 16 * HT * DI * 2;
@@ -133,7 +134,10 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(
   const int part = (int)(blockIdx.x - q * blocks_per_query) * kWaves + wave;
   const int64_t b = q / n_tokens;
   const int64_t t = q - b * n_tokens;
-  int64_t vis = (start_pos + t + 1) / ratio;
+  // position of the token: the call's start_pos, or read on the device
+  const int64_t base = pos != nullptr ? (int64_t)pos[b] : start_pos;
+  int64_t vis = (base + t + 1) / ratio;
+  vis = vis < 0 ? 0 : vis;
   const int live_end = (int)(vis < n_rows ? vis : n_rows);
   const int nbt = (n_rows + 15) / 16;     // 16-key blocks in the row
   const int nbv = (live_end + 15) / 16;   // ... with a visible key
@@ -240,13 +244,13 @@ template <int DI, int NT>
 hipError_t dispatch_heads(int ht, dim3 grid, hipStream_t s, const uint16_t* qI,
                           const uint16_t* kI, int64_t kI_bs, const float* w,
                           const uint8_t* cand, int32_t cand_width, int32_t cand_block,
-                          int32_t n_tokens, int64_t start_pos, int32_t ratio,
-                          int32_t n_heads, int32_t n_rows, float* scores, int64_t scores_ld,
-                          int32_t bpq) {
+                          int32_t n_tokens, int64_t start_pos, const int32_t* pos,
+                          int32_t ratio, int32_t n_heads, int32_t n_rows, float* scores,
+                          int64_t scores_ld, int32_t bpq) {
 #define V41_IDX_LAUNCH(HT_)                                                                   \
   hipLaunchKernelGGL((indexer_kernel<DI, HT_, NT>), grid, dim3(kThreads), 0, s, qI, kI,      \
-                     kI_bs, w, cand, cand_width, cand_block, n_tokens, start_pos, ratio,     \
-                     n_heads, n_rows, scores, scores_ld, bpq)
+                     kI_bs, w, cand, cand_width, cand_block, n_tokens, start_pos, pos,       \
+                     ratio, n_heads, n_rows, scores, scores_ld, bpq)
   switch (ht) {
     case 1: V41_IDX_LAUNCH(1); break;
     case 2: V41_IDX_LAUNCH(2); break;
@@ -261,15 +265,15 @@ template <int DI>
 hipError_t dispatch_nt(bool nt, int ht, dim3 grid, hipStream_t s, const uint16_t* qI,
                        const uint16_t* kI, int64_t kI_bs, const float* w, const uint8_t* cand,
                        int32_t cand_width, int32_t cand_block, int32_t n_tokens,
-                       int64_t start_pos, int32_t ratio, int32_t n_heads, int32_t n_rows,
-                       float* scores, int64_t scores_ld, int32_t bpq) {
+                       int64_t start_pos, const int32_t* pos, int32_t ratio, int32_t n_heads,
+                       int32_t n_rows, float* scores, int64_t scores_ld, int32_t bpq) {
   if (nt)
     return dispatch_heads<DI, 1>(ht, grid, s, qI, kI, kI_bs, w, cand, cand_width, cand_block,
-                                 n_tokens, start_pos, ratio, n_heads, n_rows, scores,
+                                 n_tokens, start_pos, pos, ratio, n_heads, n_rows, scores,
                                  scores_ld, bpq);
   return dispatch_heads<DI, 0>(ht, grid, s, qI, kI, kI_bs, w, cand, cand_width, cand_block,
-                               n_tokens, start_pos, ratio, n_heads, n_rows, scores, scores_ld,
-                               bpq);
+                               n_tokens, start_pos, pos, ratio, n_heads, n_rows, scores,
+                               scores_ld, bpq);
 }
 
 }  // namespace
@@ -277,9 +281,9 @@ hipError_t dispatch_nt(bool nt, int ht, dim3 grid, hipStream_t s, const uint16_t
 hipError_t launch_indexer_scores(const uint16_t* qI, const uint16_t* kI, int64_t kI_bs,
                                  const float* w, const uint8_t* cand, int32_t cand_width,
                                  int32_t cand_block, int32_t batch, int32_t n_tokens,
-                                 int64_t start_pos, int32_t ratio, int32_t n_heads,
-                                 int32_t head_dim, int64_t n_rows, float* scores,
-                                 int64_t scores_ld, hipStream_t s) {
+                                 int64_t start_pos, const int32_t* pos, int32_t ratio,
+                                 int32_t n_heads, int32_t head_dim, int64_t n_rows,
+                                 float* scores, int64_t scores_ld, hipStream_t s) {
   const int64_t nq = (int64_t)batch * n_tokens;
   if (nq == 0 || n_rows == 0) return hipSuccess;
   // Workgroups per query: about 384 over the whole grid (1.5 per CU; up to 3
@@ -299,15 +303,15 @@ hipError_t launch_indexer_scores(const uint16_t* qI, const uint16_t* kI, int64_t
   switch (head_dim) {
     case 32:
       return dispatch_nt<32>(nt, ht, grid, s, qI, kI, kI_bs, w, cand, cand_width, cand_block,
-                             n_tokens, start_pos, ratio, n_heads, rows, scores, scores_ld,
+                             n_tokens, start_pos, pos, ratio, n_heads, rows, scores, scores_ld,
                              (int32_t)bpq);
     case 64:
       return dispatch_nt<64>(nt, ht, grid, s, qI, kI, kI_bs, w, cand, cand_width, cand_block,
-                             n_tokens, start_pos, ratio, n_heads, rows, scores, scores_ld,
+                             n_tokens, start_pos, pos, ratio, n_heads, rows, scores, scores_ld,
                              (int32_t)bpq);
     default:
       return dispatch_nt<128>(nt, ht, grid, s, qI, kI, kI_bs, w, cand, cand_width, cand_block,
-                              n_tokens, start_pos, ratio, n_heads, rows, scores, scores_ld,
+                              n_tokens, start_pos, pos, ratio, n_heads, rows, scores, scores_ld,
                               (int32_t)bpq);
   }
 }

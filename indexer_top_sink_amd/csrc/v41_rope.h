@@ -25,6 +25,24 @@ struct RopeRowsArgs {
   int64_t ring_bs;
 };
 
+// The front of a decode step (q tails rotated in place, kv rows through the
+// rotation and fp8 into their ring slots, window indices), positions on the
+// device.  table NULL: no rotation.
+struct DecodeFrontArgs {
+  uint16_t* q;
+  const uint16_t* kv;
+  uint16_t* ring;
+  int64_t ring_bs;
+  int32_t* idx;
+  int64_t idx_ld;
+  const int32_t* pos;
+  const float* table;
+  int64_t table_rows;
+  int32_t batch, n_heads, row_len, window, rope_dim;
+};
+
+hipError_t launch_decode_front(const DecodeFrontArgs& a, hipStream_t s);
+
 hipError_t launch_rope_table(double theta, int32_t rope_dim, int64_t n_pos, float* table,
                              hipStream_t s);
 hipError_t launch_rope_rows(const RopeRowsArgs& a, hipStream_t s);

@@ -132,6 +132,94 @@ __global__ __launch_bounds__(kThreads) void rope_table_kernel(double theta, int3
   }
 }
 
+// The front of a decode step in one launch, three kinds of workgroups told
+// apart by blockIdx (each kind a contiguous range, so a workgroup's branch is
+// uniform): [q tails rotated in place | new kv rows (rotated when a table is
+// given) through fp8 into ring slot pos[b] mod W | the ring's window indices,
+// oldest first].  Every position is read on the device.  A sequence whose
+// position is negative (or, with a table, past its end) writes no kv row and
+// gets an all -1 window; its q is not rotated.
+struct FrontParams {
+  uint16_t* q;
+  const uint16_t* kv;
+  uint16_t* ring;
+  int64_t ring_bs;
+  int32_t* idx;
+  int64_t idx_ld;
+  const int32_t* pos;
+  const float* table;
+  int64_t table_rows;
+  int32_t batch, n_heads, row_len, window, rope_dim;
+  int32_t q_blocks, kv_blocks;
+};
+
+__global__ __launch_bounds__(kThreads) void decode_front_kernel(FrontParams p) {
+  int32_t blk = (int32_t)blockIdx.x;
+  const int32_t half = p.rope_dim / 2;
+  const int32_t rot0 = (p.row_len - p.rope_dim) / 8;
+  if (blk < p.q_blocks) {
+    // q: rope_dim / 8 chunks per head row
+    const int32_t chunks = p.rope_dim / 8;
+    const int32_t g = blk * kThreads + (int32_t)threadIdx.x;
+    if (g < p.batch * p.n_heads * chunks) {
+      const int32_t r = g / chunks;
+      const int32_t c = rot0 + (g - r * chunks);
+      const int32_t b = r / p.n_heads;
+      const int64_t ps = p.pos[b];
+      if (ps >= 0 && ps < p.table_rows) {
+        uint16_t* at = p.q + (int64_t)r * p.row_len + c * 8;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(at);
+        *reinterpret_cast<u32x4*>(at) =
+            rotate_chunk(v, p.table + (ps * half + (c - rot0) * 4) * 2, 1.0f);
+      }
+    }
+    return;
+  }
+  blk -= p.q_blocks;
+  if (blk < p.kv_blocks) {
+    // kv: row_len / 8 chunks per row, a multiple of 4, so a lane quad
+    // (one fp8 block) shares its row and position
+    const int32_t cpr = p.row_len / 8;
+    const int32_t g = blk * kThreads + (int32_t)threadIdx.x;
+    const bool in_range = g < p.batch * cpr;
+    const int32_t b = in_range ? g / cpr : 0;
+    const int32_t c = in_range ? g - b * cpr : 0;
+    const int64_t ps = p.pos[b];
+    const bool live = in_range && ps >= 0 && (p.table == nullptr || ps < p.table_rows);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (live) {
+      v = *reinterpret_cast<const u32x4*>(p.kv + (int64_t)b * p.row_len + c * 8);
+      if (p.table != nullptr && c >= rot0)
+        v = rotate_chunk(v, p.table + (ps * half + (c - rot0) * 4) * 2, 1.0f);
+    }
+    const uint32_t m = quad_max(chunk_amax_bits(v));
+    float s, inv_s;
+    fp8_block_scale(m, s, inv_s);
+    v = fp8_round_chunk(v, inv_s, s);
+    if (live) {
+      const int64_t slot = ps % p.window;
+      *reinterpret_cast<u32x4*>(p.ring + b * p.ring_bs + slot * p.row_len + c * 8) = v;
+    }
+    return;
+  }
+  blk -= p.kv_blocks;
+  // window indices: the whole ring oldest first once it has wrapped, else
+  // slots 0 .. pos then -1
+  const int32_t g = blk * kThreads + (int32_t)threadIdx.x;
+  if (g < p.batch * p.window) {
+    const int32_t b = g / p.window;
+    const int32_t c = g - b * p.window;
+    const int64_t ps = p.pos[b];
+    const bool live = ps >= 0 && (p.table == nullptr || ps < p.table_rows);
+    int32_t v = -1;
+    if (live) {
+      if (ps >= p.window - 1) v = (int32_t)((ps + 1 + c) % p.window);
+      else v = (c <= ps) ? c : -1;
+    }
+    p.idx[(int64_t)b * p.idx_ld + c] = v;
+  }
+}
+
 unsigned grid_for(int64_t lanes, int64_t cap) {
   int64_t blocks = (lanes + kThreads - 1) / kThreads;
   if (blocks > cap) blocks = cap;
@@ -183,6 +271,38 @@ hipError_t launch_rope_rows(const RopeRowsArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(rope_rows_kernel<true>, dim3(grid), dim3(kThreads), 0, s, p);
   else
     hipLaunchKernelGGL(rope_rows_kernel<false>, dim3(grid), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace v41
+
+namespace v41 {
+
+hipError_t launch_decode_front(const DecodeFrontArgs& a, hipStream_t s) {
+  if (a.batch == 0) return hipSuccess;
+  FrontParams p;
+  p.q = a.q;
+  p.kv = a.kv;
+  p.ring = a.ring;
+  p.ring_bs = a.ring_bs;
+  p.idx = a.idx;
+  p.idx_ld = a.idx_ld;
+  p.pos = a.pos;
+  p.table = a.table;
+  p.table_rows = a.table_rows;
+  p.batch = a.batch;
+  p.n_heads = a.n_heads;
+  p.row_len = a.row_len;
+  p.window = a.window;
+  p.rope_dim = a.table != nullptr ? a.rope_dim : 0;
+  const int64_t q_lanes = a.table != nullptr ? (int64_t)a.batch * a.n_heads * (a.rope_dim / 8) : 0;
+  const int64_t kv_lanes = (int64_t)a.batch * (a.row_len / 8);
+  const int64_t w_lanes = (int64_t)a.batch * a.window;
+  p.q_blocks = (int32_t)((q_lanes + kThreads - 1) / kThreads);
+  p.kv_blocks = (int32_t)((kv_lanes + kThreads - 1) / kThreads);
+  const int64_t w_blocks = (w_lanes + kThreads - 1) / kThreads;
+  const int64_t grid = p.q_blocks + p.kv_blocks + w_blocks;
+  hipLaunchKernelGGL(decode_front_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

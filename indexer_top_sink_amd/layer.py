@@ -159,6 +159,33 @@ def decode_step(buf: DecodeBuffers, pos: int, stream=None, rope: RopeTable | Non
                              buf.workspace, ws_bytes, stream=stream)
 
 
+def decode_step_args(buf: DecodeBuffers, pos_dev: torch.Tensor,
+                     rope: RopeTable | None = None) -> "v41.DecodeStepArgs":
+    """The argument block of v41_decode_step for these buffers: positions
+    from the device tensor pos_dev (int32 [B]), so that a graph captured
+    around the call serves every later step."""
+    g = buf.geo
+    D, W = g.head_dim, g.window
+    return v41.DecodeStepArgs.make(
+        batch=buf.batch, n_heads=g.n_heads, head_dim=D, window=W, ratio=g.ratio,
+        index_heads=g.index_heads, index_dim=g.index_dim, topk=g.topk,
+        rope_dim=rope.rope_dim if rope is not None else 0, scale=g.scale,
+        n_rows=buf.n_rows if g.ratio > 0 else 0,
+        rope_rows=rope.n_pos if rope is not None else 0,
+        ring_bs=W * D, latent_bs=buf.latent.shape[1] * D, kI_bs=buf.kI.shape[1] * g.index_dim,
+        workspace_bytes=buf.workspace.numel() if buf.workspace is not None else 0,
+        pos=pos_dev, q=buf.q, kv_new=buf.kv_new, ring=buf.ring, latent=buf.latent, kI=buf.kI,
+        qI=buf.qI, w=buf.w, rope_table=rope.table if rope is not None else None, sink=buf.sink,
+        scores=buf.scores, idx=buf.idx, out=buf.out, workspace=buf.workspace)
+
+
+def decode_step_fused(buf: DecodeBuffers, pos_dev: torch.Tensor, rope: RopeTable | None = None,
+                      stream=None) -> None:
+    """The same decode step as decode_step, as one v41_decode_step call (fewer
+    launches; every position read on the device)."""
+    v41.v41_decode_step(decode_step_args(buf, pos_dev, rope), stream=stream)
+
+
 @dataclass
 class PrefillBuffers:
     """Device state of one sequence's prefill chunk of T tokens at position 0."""

@@ -18,7 +18,35 @@ V41_OK, V41_EINVAL, V41_EHIP, V41_EDEVICE = 0, -1, -2, -3
 EXPORTS = ("v41_last_error", "v41_abi_version", "v41_fp8_round_rows", "v41_window_idx",
            "v41_indexer_scores", "v41_topk_select", "v41_sparse_attn_sink",
            "v41_sparse_attn_workspace_bytes", "v41_rope_table", "v41_rope_rows",
-           "v41_rope_fp8_rows")
+           "v41_rope_fp8_rows", "v41_decode_step")
+
+
+class DecodeStepArgs(C.Structure):
+    """v41_decode_step_args of include/v41.h, field for field."""
+    _fields_ = [("batch", C.c_int32), ("n_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("window", C.c_int32), ("ratio", C.c_int32), ("index_heads", C.c_int32),
+                ("index_dim", C.c_int32), ("topk", C.c_int32), ("rope_dim", C.c_int32),
+                ("scale", C.c_float), ("n_rows", C.c_int64), ("rope_rows", C.c_int64),
+                ("ring_bs", C.c_int64), ("latent_bs", C.c_int64), ("kI_bs", C.c_int64),
+                ("workspace_bytes", C.c_int64), ("pos", C.c_void_p), ("q", C.c_void_p),
+                ("kv_new", C.c_void_p), ("ring", C.c_void_p), ("latent", C.c_void_p),
+                ("kI", C.c_void_p), ("qI", C.c_void_p), ("w", C.c_void_p),
+                ("rope_table", C.c_void_p), ("sink", C.c_void_p), ("scores", C.c_void_p),
+                ("idx", C.c_void_p), ("out", C.c_void_p), ("workspace", C.c_void_p)]
+
+    _POINTERS = ("pos", "q", "kv_new", "ring", "latent", "kI", "qI", "w", "rope_table", "sink",
+                 "scores", "idx", "out", "workspace")
+
+    @classmethod
+    def make(cls, **kw) -> "DecodeStepArgs":
+        """Fields by name; tensors (or ints, or None) for the pointer fields."""
+        a = cls()
+        for k, v in kw.items():
+            if k in cls._POINTERS:
+                setattr(a, k, _ptr(v))
+            else:
+                setattr(a, k, v)
+        return a
 
 
 class V41Error(RuntimeError):
@@ -66,6 +94,8 @@ def load() -> C.CDLL:
     L.v41_rope_fp8_rows.restype = C.c_int
     L.v41_rope_fp8_rows.argtypes = [vp, i64, vp, i64, i32, i32, i32, i32, vp, i64, vp, i64,
                                     vp, i32, i64, vp]
+    L.v41_decode_step.restype = C.c_int
+    L.v41_decode_step.argtypes = [C.POINTER(DecodeStepArgs), vp]
     _lib = L
     return L
 
@@ -163,3 +193,7 @@ def v41_rope_fp8_rows(inp, in_ld, out, out_ld, batch, n_tokens, row_len, rope_di
                                     row_len, rope_dim, _ptr(table), table_rows, _ptr(pos),
                                     start_pos, _ptr(ring), ring_slots, ring_bs,
                                     _stream(stream)))
+
+
+def v41_decode_step(args: DecodeStepArgs, stream=None) -> None:
+    _check(load().v41_decode_step(C.byref(args), _stream(stream)))

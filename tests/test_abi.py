@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib.v41_abi_version() == 2
+    assert lib.v41_abi_version() == 3
 
 
 def _err(lib):
@@ -144,3 +144,59 @@ def test_rope_fp8_rows_rejects_bad_shapes(lib):
     # ring overlapping the input rows
     assert lib.v41_rope_fp8_rows(1 << 20, 64, None, 64, 1, 4, 64, 16, 8192, 10, None, 0,
                                  (1 << 20) + 256, 8, 512, None) == -1 and "overlaps" in _err(lib)
+
+
+def test_decode_step_args_layout_matches_header(tmp_path):
+    """The ctypes mirror of v41_decode_step_args has the C compiler's size and
+    field offsets (a small C program built against include/v41.h prints them)."""
+    import ctypes
+    import subprocess
+
+    from indexer_top_sink_amd import v41
+    fields = [f for f, _ in v41.DecodeStepArgs._fields_]
+    src = ["#include <stdio.h>", "#include <stddef.h>", '#include "v41.h"', "int main(void) {",
+           '  printf("%zu\\n", sizeof(v41_decode_step_args));']
+    src += [f'  printf("%zu\\n", offsetof(v41_decode_step_args, {f}));' for f in fields]
+    src += ["  return 0;", "}"]
+    c = tmp_path / "layout.c"
+    c.write_text("\n".join(src) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(c), "-o",
+                    str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(v41.DecodeStepArgs)
+    for f, off in zip(fields, got[1:]):
+        assert getattr(v41.DecodeStepArgs, f).offset == off, f
+
+
+def _step_args(**over):
+    from indexer_top_sink_amd import v41
+    base = dict(batch=2, n_heads=64, head_dim=512, window=128, ratio=4, index_heads=64,
+                index_dim=128, topk=512, rope_dim=0, scale=0.04, n_rows=1024, rope_rows=0,
+                ring_bs=128 * 512, latent_bs=1024 * 512, kI_bs=1024 * 128, workspace_bytes=0,
+                pos=1 << 20, q=2 << 20, kv_new=3 << 20, ring=4 << 20, latent=5 << 20,
+                kI=6 << 20, qI=7 << 20, w=8 << 20, rope_table=None, sink=9 << 20,
+                scores=10 << 20, idx=11 << 20, out=12 << 20, workspace=None)
+    base.update(over)
+    return v41.DecodeStepArgs.make(**base)
+
+
+def test_decode_step_rejects_bad_arguments(lib):
+    import ctypes
+    cases = [
+        (dict(pos=None), "NULL pos"),
+        (dict(head_dim=320), "head_dim"),
+        (dict(topk=2000), "selection limit"),
+        (dict(rope_dim=64), "rope_table"),
+        (dict(rope_dim=12, rope_table=13 << 20, rope_rows=10), "rope_dim"),
+        (dict(ring_bs=100), "ring_bs"),
+        (dict(latent=None), "no latent cache"),
+        (dict(index_dim=96), "index_dim"),
+        (dict(q=(2 << 20) + 4), "aligned"),
+    ]
+    for over, msg in cases:
+        a = _step_args(**over)
+        rc = lib.v41_decode_step(ctypes.byref(a), None)
+        assert rc == -1 and msg in _err(lib), (over, _err(lib))
+    assert lib.v41_decode_step(None, None) == -1
