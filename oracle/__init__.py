@@ -60,6 +60,8 @@ def lib():
         L.ora_rope_rows.argtypes = [u16p, u16p, C.c_int64, C.c_int32, C.c_int32, f32p,
                                     C.POINTER(C.c_int64), C.c_int32]
         L.ora_rope_rows.restype = C.c_int
+        L.ora_candidate_blocks_one.argtypes = [f64p, C.c_int64, C.c_int32, C.c_int32, u8p]
+        L.ora_candidate_blocks_one.restype = C.c_int64
         _lib = L
     return _lib
 
@@ -285,3 +287,24 @@ def rope_fp8_rows(x: np.ndarray, table: np.ndarray, row_pos, rope_dim: int) -> n
     """The window-key epilogue: RoPE on the last rope_dim values (bf16 out),
     then the fp8 round trip of the whole row (W_{t,448:} <- R_t w; W <- FP8(W))."""
     return fp8_round_rows(rope_rows(x, table, row_pos, rope_dim))
+
+
+# ---------------------------------------------------------------- candidate blocks
+def candidate_blocks(scores: np.ndarray, cand_block: int, topk_blocks: int) -> np.ndarray:
+    """scores [R, L] (converted exactly to double) -> u8 mask [R, ceil(L /
+    cand_block)]: 1 for the topk_blocks blocks with the largest block score
+    (the largest valid score of the block's positions), ties to the lower
+    block, blocks with no valid score never chosen."""
+    if cand_block < 1 or topk_blocks < 1:
+        raise ValueError("cand_block and topk_blocks must be positive")
+    s = _c(np.asarray(scores, dtype=np.float64), np.float64)
+    R, L = s.shape
+    nb = -(-L // cand_block)
+    out = np.zeros((R, nb), dtype=np.uint8)
+    for r in range(R):
+        m = lib().ora_candidate_blocks_one(s[r].ctypes.data_as(C.POINTER(C.c_double)), L,
+                                           cand_block, topk_blocks,
+                                           out[r].ctypes.data_as(C.POINTER(C.c_uint8)))
+        if m < 0:
+            raise ValueError("cand_block and topk_blocks must be positive")
+    return out

@@ -3,7 +3,8 @@
  * attention: the fp8 round trip of kv rows, the window selection, the indexer
  * score, the index top-k and the sparse attention with a per-head sink, and
  * the rotary embedding (its table and the rotation) that the kv rows and the
- * queries go through before the path.
+ * queries go through before the path, and the candidate-block selection
+ * that produces the block mask the indexer takes.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * CPU-baseline leg of the benchmark may load this library.  The GPU library
@@ -41,6 +42,8 @@
  *  - Index values outside [0, rows_a_len + rows_b_len) are skipped like -1.
  *  - The RoPE table is cos/sin of p * theta^(-2i/rope_dim), rounded once to
  *    binary32; the rotation's binary32 products are not fused.
+ *  - A candidate block's score is the largest valid score of its positions;
+ *    the blocks are chosen by the index top-k's rule.
  */
 #include <math.h>
 #include <stdint.h>
@@ -525,4 +528,62 @@ int ora_rope_rows(const uint16_t *in, uint16_t *out, int64_t rows,
         }
     }
     return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* candidate blocks (the candidate-source layer's block-level mask)     */
+/* ------------------------------------------------------------------ */
+
+/*
+ * The candidate-source layer publishes a block-level candidate mask that
+ * later index sources apply ("attn_v41" module page and "attn_v41.rs":
+ * SharedV41.candidates [queries][cand_width]; a candidate-block top-k
+ * selection beside the index top-k; config candidate_topk_blocks = 2048,
+ * candidate_block_size = 8 on the "Compressed sparse attention" layer page).
+ *
+ * Readings (the pages name the selection, not how a block is scored): block
+ * b covers compressed positions [b * cand_block, (b + 1) * cand_block) of a
+ * score row; its score is the largest score of its positions that is
+ * neither -inf nor NaN (-inf when there is none); the mask marks the
+ * topk_blocks best blocks under the index top-k's own rule (score
+ * descending, equal scores to the lower block, -inf blocks never chosen).
+ * Block scores are maxima of the given scores, so no arithmetic enters.
+ *
+ * scores: [n] doubles; mask: [ceil(n / cand_block)] bytes, 1 = candidate.
+ * Returns the number of candidate blocks, or -1 on a bad argument or an
+ * allocation failure.
+ */
+int64_t ora_candidate_blocks_one(const double *scores, int64_t n,
+                                 int32_t cand_block, int32_t topk_blocks,
+                                 uint8_t *mask)
+{
+    if (cand_block < 1 || topk_blocks < 1 || n < 0)
+        return -1;
+    int64_t nb = (n + cand_block - 1) / cand_block;
+    double *bs = (double *)malloc(sizeof(double) * (size_t)(nb > 0 ? nb : 1));
+    int32_t *sel = (int32_t *)malloc(sizeof(int32_t) * (size_t)topk_blocks);
+    if (bs == NULL || sel == NULL) {
+        free(bs);
+        free(sel);
+        return -1;
+    }
+    for (int64_t b = 0; b < nb; ++b) {
+        double m = -INFINITY;
+        for (int64_t j = b * cand_block; j < n && j < (b + 1) * cand_block; ++j) {
+            double s = scores[j];
+            if (!isnan(s) && s > m)
+                m = s;
+        }
+        bs[b] = m;
+    }
+    int64_t got = ora_topk_one(bs, nb, topk_blocks, 0, sel);
+    if (got >= 0) {
+        memset(mask, 0, (size_t)nb);
+        for (int32_t i = 0; i < topk_blocks; ++i)
+            if (sel[i] >= 0)
+                mask[sel[i]] = 1;
+    }
+    free(bs);
+    free(sel);
+    return got;
 }
