@@ -267,6 +267,24 @@ def algorithmic(wl, host_idx=None, valid_pairs=None, rope=False):
     return k
 
 
+def time_candidate_blocks(torch, device, steps):
+    """The candidate-source selection at decode16's shape: 16 score rows of
+    32768 positions, the best 2048 of 4096 blocks of 8.  Per-launch us and the
+    algorithmic bytes (scores read once, one mask byte per block written)."""
+    from inputs import synth
+    from indexer_top_sink_amd import v41
+    R, L, cb, kb = 16, 32768, 8, 2048
+    s = torch.from_numpy(synth.normal_f32(0x5EED4999, synth.TAG_MISC, (R, L))).to(device)
+    cand = torch.empty(R, L // cb, dtype=torch.uint8, device=device)
+    fn = lambda: v41.v41_candidate_blocks(s, R, L, L, cb, kb, cand, L // cb)
+    g = capture([fn] * 8, torch)
+    us = time_replays([g], max(4, steps // 8), torch) * 1e3 / 8
+    nbytes = R * L * 4 + R * (L // cb)
+    return {"shape": f"{R} rows x {L} positions, top {kb} of {L // cb} blocks of {cb}",
+            "avg_us": round(us, 2), "algorithmic_bytes": nbytes,
+            "achieved_GBs": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
 # ----------------------------------------------------------------- CPU baseline
 def cpu_baseline(wl, n_sample, budget_s=30.0):
     """The oracle (plain C, one thread) on the first sequences / tokens of the
@@ -532,6 +550,18 @@ def main():
                 "indexer_roofline": roofline_entry("indexer_scores", pwork,
                                                    pk["indexer_scores"], "mfma", pw.name),
                 "kernels_us": {k: round(v, 2) for k, v in pk.items()}}}
+    if not args.no_secondary and wl.name != "decode1":
+        # one sequence at context 4096: the step's latency floor
+        lw, lms, lk, _, lsep = run_workload("decode1", args.steps, args.warmup,
+                                            args.input_sets, torch, device,
+                                            separate=args.separate_calls)
+        out.setdefault("secondary", {})["decode1_latency"] = {
+            "us_per_step": round(lms * 1e3, 2),
+            "us_per_step_separate_calls": round(lsep * 1e3, 2) if lsep is not None else None,
+            "kernels_us": {k: round(v, 2) for k, v in lk.items()}}
+    if not args.no_secondary:
+        out.setdefault("secondary", {})["candidate_blocks"] = time_candidate_blocks(
+            torch, device, args.steps)
     if not args.no_secondary and not args.rope:
         # the same step with the rotary epilogue in front (pre-rotation q and kv)
         rw, rms, rk, rwork, rsep = run_workload(wl.name, args.steps, args.warmup,

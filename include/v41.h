@@ -53,6 +53,8 @@ typedef void *v41_stream;
 #define V41_MAX_WIDTH 2048
 /* Largest indexer head count one call takes. */
 #define V41_MAX_INDEX_HEADS 64
+/* Most candidate blocks per score row one v41_candidate_blocks call takes. */
+#define V41_MAX_CAND_BLOCKS 32768
 
 /* Message for the last non-zero status on this thread ("" if none). */
 const char *v41_last_error(void);
@@ -152,6 +154,30 @@ int v41_indexer_scores(const v41_bf16 *qI, const v41_bf16 *kI, int64_t kI_bs,
 int v41_topk_select(const float *scores, int64_t n_sel_rows, int64_t n_cols,
                     int64_t scores_ld, int32_t k, int32_t offset, int32_t *idx,
                     int64_t idx_ld, v41_stream stream);
+
+/*
+ * Candidate-block selection: the block-level candidate mask that the
+ * candidate-source layer publishes and later index sources apply ("attn_v41"
+ * module page: the candidate-block top-k selection; "attn_v41.rs":
+ * SharedV41.candidates [queries][cand_width]; config candidate_block_size 8,
+ * candidate_topk_blocks 2048).  The result is the `cand` input of
+ * v41_indexer_scores.
+ *
+ * Per score row: block b covers positions [b * cand_block, (b + 1) *
+ * cand_block); its score is the largest score of those positions that is
+ * neither -inf nor NaN (the pages do not state the block score: this is the
+ * reading taken).  The topk_blocks best blocks (score descending, equal
+ * scores, +0 equal to -0, to the lower block; blocks with no valid score are
+ * never chosen) get cand = 1, every other block 0.
+ *
+ *   scores  f32 [n_sel_rows][scores_ld], n_cols <= scores_ld
+ *   cand    u8 [n_sel_rows][cand_ld]; the first ceil(n_cols / cand_block)
+ *           bytes of each row are written, at most V41_MAX_CAND_BLOCKS
+ *   cand_block, topk_blocks >= 1
+ */
+int v41_candidate_blocks(const float *scores, int64_t n_sel_rows, int64_t n_cols,
+                         int64_t scores_ld, int32_t cand_block, int32_t topk_blocks,
+                         uint8_t *cand, int64_t cand_ld, v41_stream stream);
 
 /*
  * Sparse attention with the sink ("Compressed sparse attention", All 25

@@ -63,7 +63,7 @@ extern "C" {
 
 const char* v41_last_error(void) { return g_err; }
 
-int v41_abi_version(void) { return 3; }
+int v41_abi_version(void) { return 4; }
 
 int v41_fp8_round_rows(const v41_bf16* in, int64_t in_ld, v41_bf16* out, int64_t out_ld,
                        int64_t rows, int32_t row_len, v41_bf16* ring, int32_t ring_slots,
@@ -353,6 +353,29 @@ int v41_rope_fp8_rows(const v41_bf16* in, int64_t in_ld, v41_bf16* out, int64_t 
                       table, table_rows, pos, start_pos, false, true, ring,
                       ring != nullptr ? ring_slots : 0, ring_bs};
   return launched(v41::launch_rope_rows(a, (hipStream_t)stream), "rope_fp8_rows");
+}
+
+int v41_candidate_blocks(const float* scores, int64_t n_sel_rows, int64_t n_cols,
+                         int64_t scores_ld, int32_t cand_block, int32_t topk_blocks,
+                         uint8_t* cand, int64_t cand_ld, v41_stream stream) {
+  if (n_sel_rows < 0 || n_cols < 0) return fail(V41_EINVAL, "candidate_blocks: negative size");
+  if (cand_block < 1) return fail(V41_EINVAL, "candidate_blocks: cand_block < 1");
+  if (topk_blocks < 1) return fail(V41_EINVAL, "candidate_blocks: topk_blocks < 1");
+  if (scores_ld < n_cols) return fail(V41_EINVAL, "candidate_blocks: scores_ld < n_cols");
+  if (n_cols >= 0x7FFFFFFFLL) return fail(V41_EINVAL, "candidate_blocks: n_cols too large");
+  const int64_t nb = (n_cols + cand_block - 1) / cand_block;
+  if (nb > V41_MAX_CAND_BLOCKS)
+    return fail(V41_EINVAL, "candidate_blocks: %lld blocks exceed %d", (long long)nb,
+                V41_MAX_CAND_BLOCKS);
+  if (cand_ld < nb) return fail(V41_EINVAL, "candidate_blocks: cand_ld < number of blocks");
+  if (n_sel_rows > 0 && nb > 0 && (scores == nullptr || cand == nullptr))
+    return fail(V41_EINVAL, "candidate_blocks: NULL scores/cand");
+  int rc = check_device();
+  if (rc) return rc;
+  return launched(v41::launch_candidate_blocks(scores, n_sel_rows, n_cols, scores_ld,
+                                               cand_block, topk_blocks, cand, cand_ld,
+                                               (hipStream_t)stream),
+                  "candidate_blocks");
 }
 
 int v41_decode_step(const v41_decode_step_args* a, v41_stream stream) {

@@ -58,6 +58,10 @@ hipError_t launch_topk_select(const float* scores, int64_t n_sel_rows, int64_t n
                               int64_t scores_ld, int32_t k, int32_t offset, int32_t* idx,
                               int64_t idx_ld, hipStream_t s);
 
+hipError_t launch_candidate_blocks(const float* scores, int64_t n_sel_rows, int64_t n_cols,
+                                   int64_t scores_ld, int32_t cand_block, int32_t topk_blocks,
+                                   uint8_t* cand, int64_t cand_ld, hipStream_t s);
+
 struct AttnArgs {
   const uint16_t* q;
   const uint16_t* rows_a;

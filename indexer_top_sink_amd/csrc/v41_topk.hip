@@ -15,11 +15,15 @@
 //     across lanes so that equal digits do not serialise on one word; two
 //     histograms alternate so clearing the next one overlaps the counting,
 //     and the first wavefront sums the copies while it scans (two barriers
-//     per pass);
+//     per pass).  The passes stop as soon as the bin holding the k-th key is
+//     taken whole (then no tie inside it needs breaking): with distinct
+//     scores that is usually after two passes;
 //  3. the selection is {key > T} plus the first `need` positions with key == T
 //     (ties to the lower position); one block-wide exclusive scan of packed
 //     (greater, equal) counts gives each thread its output slots, and the
 //     positions are written in ascending order, then -1 up to k.
+// The candidate-block selection runs the same select over per-block maxima
+// and writes a byte mask instead of positions.
 #include "v41_common.h"
 
 namespace v41 {
@@ -38,7 +42,7 @@ template <int NT>
 struct TopkShared {
   uint32_t hist[2][kHistCopies * 256];  // alternate passes; the idle one is cleared
   uint32_t red[3][NT / kWave];
-  uint32_t digit, above;
+  uint32_t digit, above, bin;
 };
 
 // Exclusive scan of one value per thread over the block (two barriers).
@@ -141,12 +145,20 @@ __device__ __forceinline__ void radix_select(ForKeys for_keys, uint32_t m, uint3
         while (j < 3 && need_r > cum + c[j]) cum += c[j++];
         sh.digit = 255 - 4 * lane - j;
         sh.above = cum;
+        sh.bin = c[j];
       }
     }
     __syncthreads();
     prefix |= sh.digit << shift;
     pmask |= 255u << shift;
     need_r -= sh.above;
+    if (need_r == sh.bin) {
+      // the whole bin is taken: the selection is every valid key with
+      // d >= prefix, and no tie inside the bin needs breaking
+      T = kmin + prefix - 1u;
+      need = 0u;
+      return;
+    }
     if (shift == 0) break;
     // the last window may overlap decided bits; they are fixed by the prefix
     shift = shift > 8 ? shift - 8 : 0;
@@ -286,7 +298,99 @@ __global__ __launch_bounds__(NT) void topk_mem_kernel(const float* __restrict__ 
   for (int32_t i = (int32_t)m + tid; i < k; i += NT) orow[i] = -1;
 }
 
+// Candidate blocks of a score row: block b covers positions [b*cb, (b+1)*cb);
+// its key is the largest key of its positions (key 0, not selectable, when
+// none is valid).  The topk_blocks best block keys are chosen exactly as the
+// index top-k chooses positions (same radix select, ties to the lower block)
+// and written as a byte mask over the ceil(n_cols / cb) blocks.  Thread t owns
+// the KPT contiguous blocks [t*KPT, (t+1)*KPT).
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) void cand_reg_kernel(const float* __restrict__ scores,
+                                                      int32_t n_cols, int64_t scores_ld,
+                                                      int32_t cb, int32_t k,
+                                                      uint8_t* __restrict__ cand,
+                                                      int64_t cand_ld) {
+  __shared__ TopkShared<NT> sh;
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const float* __restrict__ srow = scores + row * scores_ld;
+  uint8_t* __restrict__ crow = cand + row * cand_ld;
+  const int32_t nb = (n_cols + cb - 1) / cb;
+  const int32_t b0 = tid * KPT;
+
+  uint32_t key[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    uint32_t m = 0u;
+    if (b0 + i < nb) {
+      const int32_t j0 = (b0 + i) * cb;
+      const int32_t j1 = j0 + cb < n_cols ? j0 + cb : n_cols;
+      for (int32_t j = j0; j < j1; ++j) m = max(m, score_key(srow[j]));
+    }
+    key[i] = m;
+  }
+  uint32_t nv_t = 0, kmin_t = 0xFFFFFFFFu, kmax_t = 0u;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    if (key[i] != 0u) {
+      ++nv_t;
+      kmin_t = min(kmin_t, key[i]);
+      kmax_t = max(kmax_t, key[i]);
+    }
+  }
+  uint32_t nv, kmin, kmax;
+  block_stats<NT>(nv_t, kmin_t, kmax_t, sh, nv, kmin, kmax);
+  const uint32_t m = nv < (uint32_t)k ? nv : (uint32_t)k;
+  uint32_t T = 0u, need = 0u;
+  if (nv > (uint32_t)k) {
+    radix_select<NT>(
+        [&](auto f) {
+#pragma unroll
+          for (int i = 0; i < KPT; ++i) f(key[i]);
+        },
+        m, kmin, kmax, sh, T, need);
+  }
+  uint32_t ce = 0;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) ce += (need != 0u) && (key[i] == T);
+  uint32_t er = block_excl_scan<NT>(ce, sh);
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    uint8_t take = 0;
+    if (key[i] > T) {
+      take = 1;
+    } else if (need != 0u && key[i] == T) {
+      take = er < need ? 1 : 0;
+      ++er;
+    }
+    if (b0 + i < nb) crow[b0 + i] = take;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_candidate_blocks(const float* scores, int64_t n_sel_rows, int64_t n_cols,
+                                   int64_t scores_ld, int32_t cand_block, int32_t topk_blocks,
+                                   uint8_t* cand, int64_t cand_ld, hipStream_t s) {
+  if (n_sel_rows == 0) return hipSuccess;
+  const dim3 grid((unsigned)n_sel_rows);
+  const int64_t nb = (n_cols + cand_block - 1) / cand_block;
+  const int32_t nc = (int32_t)n_cols;  // the ABI bounds the block count
+#define V41_CAND(NT_, KPT_)                                                                   \
+  hipLaunchKernelGGL((cand_reg_kernel<NT_, KPT_>), grid, dim3(NT_), 0, s, scores, nc,        \
+                     scores_ld, cand_block, topk_blocks, cand, cand_ld)
+  if (nb <= 256 * 4) {
+    V41_CAND(256, 4);
+  } else if (nb <= 1024 * 4) {
+    V41_CAND(1024, 4);
+  } else if (nb <= 1024 * 16) {
+    V41_CAND(1024, 16);
+  } else {
+    V41_CAND(1024, 32);
+  }
+#undef V41_CAND
+  return hipGetLastError();
+}
 
 hipError_t launch_topk_select(const float* scores, int64_t n_sel_rows, int64_t n_cols,
                               int64_t scores_ld, int32_t k, int32_t offset, int32_t* idx,

@@ -18,7 +18,7 @@ V41_OK, V41_EINVAL, V41_EHIP, V41_EDEVICE = 0, -1, -2, -3
 EXPORTS = ("v41_last_error", "v41_abi_version", "v41_fp8_round_rows", "v41_window_idx",
            "v41_indexer_scores", "v41_topk_select", "v41_sparse_attn_sink",
            "v41_sparse_attn_workspace_bytes", "v41_rope_table", "v41_rope_rows",
-           "v41_rope_fp8_rows", "v41_decode_step")
+           "v41_rope_fp8_rows", "v41_decode_step", "v41_candidate_blocks")
 
 
 class DecodeStepArgs(C.Structure):
@@ -94,6 +94,8 @@ def load() -> C.CDLL:
     L.v41_rope_fp8_rows.restype = C.c_int
     L.v41_rope_fp8_rows.argtypes = [vp, i64, vp, i64, i32, i32, i32, i32, vp, i64, vp, i64,
                                     vp, i32, i64, vp]
+    L.v41_candidate_blocks.restype = C.c_int
+    L.v41_candidate_blocks.argtypes = [vp, i64, i64, i64, i32, i32, vp, i64, vp]
     L.v41_decode_step.restype = C.c_int
     L.v41_decode_step.argtypes = [C.POINTER(DecodeStepArgs), vp]
     _lib = L
@@ -197,3 +199,9 @@ def v41_rope_fp8_rows(inp, in_ld, out, out_ld, batch, n_tokens, row_len, rope_di
 
 def v41_decode_step(args: DecodeStepArgs, stream=None) -> None:
     _check(load().v41_decode_step(C.byref(args), _stream(stream)))
+
+
+def v41_candidate_blocks(scores, n_sel_rows, n_cols, scores_ld, cand_block, topk_blocks, cand,
+                         cand_ld, stream=None) -> None:
+    _check(load().v41_candidate_blocks(_ptr(scores), n_sel_rows, n_cols, scores_ld, cand_block,
+                                       topk_blocks, _ptr(cand), cand_ld, _stream(stream)))

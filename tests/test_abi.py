@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib.v41_abi_version() == 3
+    assert lib.v41_abi_version() == 4
 
 
 def _err(lib):
@@ -200,3 +200,13 @@ def test_decode_step_rejects_bad_arguments(lib):
         rc = lib.v41_decode_step(ctypes.byref(a), None)
         assert rc == -1 and msg in _err(lib), (over, _err(lib))
     assert lib.v41_decode_step(None, None) == -1
+
+
+def test_candidate_blocks_rejects_bad_arguments(lib):
+    assert lib.v41_candidate_blocks(1024, 1, 64, 64, 0, 4, 4096, 8, None) == -1
+    assert "cand_block" in _err(lib)
+    assert lib.v41_candidate_blocks(1024, 1, 64, 64, 8, 0, 4096, 8, None) == -1
+    assert lib.v41_candidate_blocks(1024, 1, 64, 64, 8, 4, 4096, 7, None) == -1
+    assert "cand_ld" in _err(lib)
+    assert lib.v41_candidate_blocks(1024, 1, 1 << 20, 1 << 20, 8, 4, 4096, 1 << 17,
+                                    None) == -1 and "exceed" in _err(lib)
