@@ -304,10 +304,13 @@ __global__ __launch_bounds__(NT) void topk_mem_kernel(const float* __restrict__ 
 // index top-k chooses positions (same radix select, ties to the lower block)
 // and written as a byte mask over the ceil(n_cols / cb) blocks.  Thread t owns
 // the KPT contiguous blocks [t*KPT, (t+1)*KPT).
-template <int NT, int KPT>
+// CB > 0 fixes the block size at compile time (16-byte loads, all issued
+// before the maxima are taken); CB == 0 reads a runtime block size one score
+// at a time.
+template <int NT, int KPT, int CB>
 __global__ __launch_bounds__(NT) void cand_reg_kernel(const float* __restrict__ scores,
                                                       int32_t n_cols, int64_t scores_ld,
-                                                      int32_t cb, int32_t k,
+                                                      int32_t cb_rt, int32_t k,
                                                       uint8_t* __restrict__ cand,
                                                       int64_t cand_ld) {
   __shared__ TopkShared<NT> sh;
@@ -315,19 +318,56 @@ __global__ __launch_bounds__(NT) void cand_reg_kernel(const float* __restrict__ 
   const int64_t row = blockIdx.x;
   const float* __restrict__ srow = scores + row * scores_ld;
   uint8_t* __restrict__ crow = cand + row * cand_ld;
+  const int32_t cb = CB > 0 ? CB : cb_rt;
   const int32_t nb = (n_cols + cb - 1) / cb;
   const int32_t b0 = tid * KPT;
 
   uint32_t key[KPT];
+  if constexpr (CB > 0) {
+    // whole blocks of this thread lie inside the row and start 16-byte aligned
+    const bool vec = ((reinterpret_cast<uintptr_t>(srow) & 15u) == 0) &&
+                     (b0 + KPT) * CB <= n_cols;
+    if (vec) {
+      float4 f[KPT][CB / 4];
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    uint32_t m = 0u;
-    if (b0 + i < nb) {
-      const int32_t j0 = (b0 + i) * cb;
-      const int32_t j1 = j0 + cb < n_cols ? j0 + cb : n_cols;
-      for (int32_t j = j0; j < j1; ++j) m = max(m, score_key(srow[j]));
+      for (int i = 0; i < KPT; ++i)
+#pragma unroll
+        for (int v = 0; v < CB / 4; ++v)
+          f[i][v] = *reinterpret_cast<const float4*>(srow + (b0 + i) * CB + 4 * v);
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        uint32_t m = 0u;
+#pragma unroll
+        for (int v = 0; v < CB / 4; ++v) {
+          m = max(m, score_key(f[i][v].x));
+          m = max(m, score_key(f[i][v].y));
+          m = max(m, score_key(f[i][v].z));
+          m = max(m, score_key(f[i][v].w));
+        }
+        key[i] = m;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        uint32_t m = 0u;
+        const int32_t j0 = (b0 + i) * CB;
+#pragma unroll
+        for (int j = 0; j < CB; ++j)
+          if (j0 + j < n_cols) m = max(m, score_key(srow[j0 + j]));
+        key[i] = m;
+      }
     }
-    key[i] = m;
+  } else {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      uint32_t m = 0u;
+      if (b0 + i < nb) {
+        const int32_t j0 = (b0 + i) * cb;
+        const int32_t j1 = j0 + cb < n_cols ? j0 + cb : n_cols;
+        for (int32_t j = j0; j < j1; ++j) m = max(m, score_key(srow[j]));
+      }
+      key[i] = m;
+    }
   }
   uint32_t nv_t = 0, kmin_t = 0xFFFFFFFFu, kmax_t = 0u;
 #pragma unroll
@@ -376,17 +416,20 @@ hipError_t launch_candidate_blocks(const float* scores, int64_t n_sel_rows, int6
   const dim3 grid((unsigned)n_sel_rows);
   const int64_t nb = (n_cols + cand_block - 1) / cand_block;
   const int32_t nc = (int32_t)n_cols;  // the ABI bounds the block count
-#define V41_CAND(NT_, KPT_)                                                                   \
-  hipLaunchKernelGGL((cand_reg_kernel<NT_, KPT_>), grid, dim3(NT_), 0, s, scores, nc,        \
+#define V41_CAND(NT_, KPT_, CB_)                                                              \
+  hipLaunchKernelGGL((cand_reg_kernel<NT_, KPT_, CB_>), grid, dim3(NT_), 0, s, scores, nc,   \
                      scores_ld, cand_block, topk_blocks, cand, cand_ld)
-  if (nb <= 256 * 4) {
-    V41_CAND(256, 4);
-  } else if (nb <= 1024 * 4) {
-    V41_CAND(1024, 4);
-  } else if (nb <= 1024 * 16) {
-    V41_CAND(1024, 16);
+  if (cand_block == 8) {
+    // the configured block size
+    if (nb <= 256 * 4) V41_CAND(256, 4, 8);
+    else if (nb <= 1024 * 4) V41_CAND(1024, 4, 8);
+    else if (nb <= 1024 * 16) V41_CAND(1024, 16, 0);
+    else V41_CAND(1024, 32, 0);
   } else {
-    V41_CAND(1024, 32);
+    if (nb <= 256 * 4) V41_CAND(256, 4, 0);
+    else if (nb <= 1024 * 4) V41_CAND(1024, 4, 0);
+    else if (nb <= 1024 * 16) V41_CAND(1024, 16, 0);
+    else V41_CAND(1024, 32, 0);
   }
 #undef V41_CAND
   return hipGetLastError();

@@ -42,7 +42,7 @@ def tricky_scores(seed, R, L):
 @pytest.mark.parametrize("R,L,cb,k", [(5, 200, 4, 7), (2, 13, 5, 1), (3, 1000, 8, 2048),
                                       (64, 8192, 8, 512), (16, 32768, 8, 2048),
                                       (2, 131072, 8, 2048), (1, 262144, 8, 2048),
-                                      (4, 5000, 1, 300)])
+                                      (4, 5000, 1, 300), (3, 1003, 8, 100)])
 def test_candidate_blocks_parity(v41, R, L, cb, k):
     say("candidate blocks", R, L, cb, k)
     s = tricky_scores(1000 + L, R, L)
