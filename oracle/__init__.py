@@ -62,6 +62,9 @@ def lib():
         L.ora_rope_rows.restype = C.c_int
         L.ora_candidate_blocks_one.argtypes = [f64p, C.c_int64, C.c_int32, C.c_int32, u8p]
         L.ora_candidate_blocks_one.restype = C.c_int64
+        L.ora_grouped_output.argtypes = [u16p, u16p, u16p, C.c_int64, C.c_int32, C.c_int32,
+                                         C.c_int32, C.c_int32, u16p, u16p]
+        L.ora_grouped_output.restype = None
         _lib = L
     return _lib
 
@@ -308,3 +311,24 @@ def candidate_blocks(scores: np.ndarray, cand_block: int, topk_blocks: int) -> n
         if m < 0:
             raise ValueError("cand_block and topk_blocks must be positive")
     return out
+
+
+# ---------------------------------------------------------------- grouped output
+def grouped_output(o_bar: np.ndarray, wo_a: np.ndarray, wo_b: np.ndarray, groups: int):
+    """o_bar [T, H, D] (or [T, H*D]) bf16 after the inverse rotation; wo_a
+    [groups*rank, gw]; wo_b [dim, groups*rank].  Returns (og [T, groups*rank],
+    x [T, dim]) as bf16 bits: each projection a double sum rounded once."""
+    o = _c(o_bar, np.uint16)
+    T = o.shape[0]
+    o = o.reshape(T, -1)
+    wa = _c(wo_a, np.uint16)
+    wb = _c(wo_b, np.uint16)
+    gr, gw = wa.shape
+    if gr % groups or o.shape[1] != groups * gw or wb.shape[1] != gr:
+        raise ValueError("shapes do not match the grouping")
+    og = np.empty((T, gr), dtype=np.uint16)
+    x = np.empty((T, wb.shape[0]), dtype=np.uint16)
+    lib().ora_grouped_output(_p(o, C.c_uint16), _p(wa, C.c_uint16), _p(wb, C.c_uint16), T,
+                             groups, gr // groups, gw, wb.shape[0], _p(og, C.c_uint16),
+                             _p(x, C.c_uint16))
+    return og, x

@@ -3,8 +3,9 @@
  * attention: the fp8 round trip of kv rows, the window selection, the indexer
  * score, the index top-k and the sparse attention with a per-head sink, and
  * the rotary embedding (its table and the rotation) that the kv rows and the
- * queries go through before the path, and the candidate-block selection
- * that produces the block mask the indexer takes.
+ * queries go through before the path, the candidate-block selection
+ * that produces the block mask the indexer takes, and the grouped output
+ * projection after it.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * CPU-baseline leg of the benchmark may load this library.  The GPU library
@@ -586,4 +587,58 @@ int64_t ora_candidate_blocks_one(const double *scores, int64_t n,
     free(bs);
     free(sel);
     return got;
+}
+
+/* ------------------------------------------------------------------ */
+/* grouped output projection (o^g = [O_bar_h]_{h in r} W_OA,r; D = o^g W_OB) */
+/* ------------------------------------------------------------------ */
+
+/*
+ * The output side of the layer ("Compressed sparse attention", All 25 steps,
+ * "Grouped output": o^g_{t,r} = [O_bar_{h,t}]_{h in r} W_{OA,r} and
+ * Delta = o^g W_{OB}; the model code on that page views o as [T, groups,
+ * heads*head_dim/groups] and contracts each group with its own slice of wo_a,
+ * then applies wo_b to the flattened groups; "attn_v41.rs": wo_a is
+ * [groups * o_rank, gw] and wo_b [dim, groups * o_rank], both [out, in];
+ * "deepseek_v41_ref::attn" precision paragraph: every projection accumulates
+ * in f32 and returns bf16).
+ *
+ * o_bar: [T][groups * gw] bf16 (the attention output after the inverse
+ * rotation, heads contiguous, so group g holds heads g*H/groups ..);
+ * wo_a: [groups * rank][gw]; wo_b: [dim][groups * rank];
+ * og: [T][groups * rank] bf16 out; x: [T][dim] bf16 out.
+ * og[t][g*rank + r] = sum_d o_bar[t][g*gw + d] * wo_a[g*rank + r][d], and
+ * x[t][c] = sum_j og[t][j] * wo_b[c][j] over the bf16 og, each sum taken in
+ * double and rounded once to bf16 (the f32 accumulation of the pages is the
+ * same real number up to its rounding).
+ */
+void ora_grouped_output(const uint16_t *o_bar, const uint16_t *wo_a,
+                        const uint16_t *wo_b, int64_t T, int32_t groups,
+                        int32_t rank, int32_t gw, int32_t dim, uint16_t *og,
+                        uint16_t *x)
+{
+    int64_t width = (int64_t)groups * gw;
+    int64_t og_w = (int64_t)groups * rank;
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t *ot = o_bar + t * width;
+        uint16_t *gt = og + t * og_w;
+        for (int32_t g = 0; g < groups; ++g) {
+            for (int32_t r = 0; r < rank; ++r) {
+                const uint16_t *wr = wo_a + ((int64_t)g * rank + r) * gw;
+                double acc = 0.0;
+                for (int32_t d = 0; d < gw; ++d)
+                    acc += ora_bf16_to_double(ot[(int64_t)g * gw + d]) *
+                           ora_bf16_to_double(wr[d]);
+                gt[(int64_t)g * rank + r] = ora_double_to_bf16(acc);
+            }
+        }
+        uint16_t *xt = x + t * dim;
+        for (int32_t c = 0; c < dim; ++c) {
+            const uint16_t *wc = wo_b + (int64_t)c * og_w;
+            double acc = 0.0;
+            for (int64_t j = 0; j < og_w; ++j)
+                acc += ora_bf16_to_double(gt[j]) * ora_bf16_to_double(wc[j]);
+            xt[c] = ora_double_to_bf16(acc);
+        }
+    }
 }
