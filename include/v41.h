@@ -302,6 +302,61 @@ int v41_rope_fp8_rows(const v41_bf16 *in, int64_t in_ld, v41_bf16 *out, int64_t 
                       int64_t ring_bs, v41_stream stream);
 
 /*
+ * One bf16 projection on the matrix cores ("deepseek_v41_ref::attn"
+ * precision paragraph: every projection is linear_bf16, f32 accumulation and
+ * a bf16 result; weights are [out, in]):
+ *   y_g[m][n] = sum_k a_g[m][k] * w_g[n][k]   for g < groups,
+ * with a_g = a + g * a_gs, w_g = w + g * w_gs, y_g = y + g * y_gs (element
+ * offsets).  groups > 1 is a block-diagonal projection such as wo_a (each
+ * group of heads with its own block); groups == 1 a plain one such as wo_b.
+ *
+ *   a   bf16 rows of K values, row stride lda (>= K, multiple of 8)
+ *   w   bf16 rows of K values, row stride ldw (>= K, multiple of 8)
+ *   y   bf16 [M][ldy] per group (ldy >= N)
+ *   K   a positive multiple of 64; M >= 0; N >= 1.
+ *   workspace / workspace_bytes: optional device scratch; with at least
+ *       v41_linear_workspace_bytes(...) bytes, a call with few rows (M <= 64)
+ *       splits K over workgroups (f32 partial sums added in a fixed order).
+ *       The result is the same up to f32 rounding order either way.  Calls
+ *       sharing a workspace must not overlap in time.
+ *   a, w, workspace: 16-byte aligned; a_gs and w_gs multiples of 8.
+ */
+int v41_linear_bf16(const v41_bf16 *a, int64_t lda, int64_t a_gs, const v41_bf16 *w,
+                    int64_t ldw, int64_t w_gs, v41_bf16 *y, int64_t ldy, int64_t y_gs,
+                    int32_t M, int32_t N, int32_t K, int32_t groups, void *workspace,
+                    int64_t workspace_bytes, v41_stream stream);
+
+/* Workspace size that lets v41_linear_bf16 split K as it prefers (0 when it
+ * would not split). */
+int64_t v41_linear_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t groups);
+
+/*
+ * The grouped output projection after the attention ("Compressed sparse
+ * attention", All 25 steps, "Grouped output": o^g_{t,r} = [O_bar_{h,t}]_{h in r}
+ * W_{OA,r}, then Delta = o^g W_{OB}; "attn_v41.rs": wo_a [groups * o_rank,
+ * gw], wo_b [dim, groups * o_rank]).  Two v41_linear_bf16 launches: the
+ * block-diagonal wo_a over the groups of contiguous heads, then wo_b over the
+ * bf16 o^g.  O_bar is the attention output after the inverse rotation
+ * (v41_rope_rows with inverse = 1).
+ *
+ *   o_bar  bf16 [n_tokens][n_heads][head_dim]; gw = n_heads / groups * head_dim
+ *   wo_a   bf16 [groups * rank][gw]; wo_b bf16 [dim][groups * rank]
+ *   og     bf16 [n_tokens][groups * rank] (written; the input of wo_b)
+ *   x      bf16 [n_tokens][dim]
+ *   n_heads a multiple of groups; gw and groups * rank multiples of 64.
+ *   workspace: at least v41_grouped_output_workspace_bytes(...) bytes to
+ *       split K at decode sizes (optional).
+ */
+int v41_grouped_output(const v41_bf16 *o_bar, int64_t n_tokens, int32_t n_heads,
+                       int32_t head_dim, int32_t groups, int32_t rank, int32_t dim,
+                       const v41_bf16 *wo_a, const v41_bf16 *wo_b, v41_bf16 *og, v41_bf16 *x,
+                       void *workspace, int64_t workspace_bytes, v41_stream stream);
+
+int64_t v41_grouped_output_workspace_bytes(int64_t n_tokens, int32_t n_heads,
+                                           int32_t head_dim, int32_t groups, int32_t rank,
+                                           int32_t dim);
+
+/*
  * One whole decode step in one call, with every position read on the device,
  * so that a HIP graph captured once replays it at every later step (the
  * captured decode step of "attn_v41.rs": the graph's ring_put reads pos[0]

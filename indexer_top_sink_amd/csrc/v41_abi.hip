@@ -12,6 +12,7 @@
 #include "../../include/v41.h"
 #include "v41_common.h"
 #include "v41_rope.h"
+#include "v41_gemm.h"
 
 namespace {
 
@@ -63,7 +64,7 @@ extern "C" {
 
 const char* v41_last_error(void) { return g_err; }
 
-int v41_abi_version(void) { return 4; }
+int v41_abi_version(void) { return 5; }
 
 int v41_fp8_round_rows(const v41_bf16* in, int64_t in_ld, v41_bf16* out, int64_t out_ld,
                        int64_t rows, int32_t row_len, v41_bf16* ring, int32_t ring_slots,
@@ -376,6 +377,99 @@ int v41_candidate_blocks(const float* scores, int64_t n_sel_rows, int64_t n_cols
                                                cand_block, topk_blocks, cand, cand_ld,
                                                (hipStream_t)stream),
                   "candidate_blocks");
+}
+
+namespace {
+
+int check_linear(const char* who, const v41_bf16* a, int64_t lda, int64_t a_gs,
+                 const v41_bf16* w, int64_t ldw, int64_t w_gs, const v41_bf16* y,
+                 int64_t ldy, int64_t y_gs, int32_t M, int32_t N, int32_t K, int32_t groups,
+                 const void* workspace, int64_t workspace_bytes) {
+  if (M < 0 || N < 1 || groups < 1) return fail(V41_EINVAL, "%s: M < 0, N < 1 or groups < 1", who);
+  if (K < 64 || K % 64 != 0) return fail(V41_EINVAL, "%s: K %d is not a positive multiple of 64",
+                                         who, K);
+  if (lda < K || ldw < K || ldy < N)
+    return fail(V41_EINVAL, "%s: lda/ldw must be >= K and ldy >= N", who);
+  if (lda % 8 != 0 || ldw % 8 != 0 || a_gs % 8 != 0 || w_gs % 8 != 0)
+    return fail(V41_EINVAL, "%s: lda, ldw, a_gs and w_gs must be multiples of 8", who);
+  if (groups > 1 && (a_gs < 0 || w_gs < (int64_t)N * ldw - (ldw - K) || y_gs < 0))
+    return fail(V41_EINVAL, "%s: group strides out of range", who);
+  if ((int64_t)groups * M * N >= ((int64_t)1 << 40))
+    return fail(V41_EINVAL, "%s: output too large", who);
+  if (M > 0 && (a == nullptr || w == nullptr || y == nullptr))
+    return fail(V41_EINVAL, "%s: NULL a/w/y", who);
+  if (!aligned16(a) || !aligned16(w) || !aligned16(workspace))
+    return fail(V41_EINVAL, "%s: a, w and workspace must be 16-byte aligned", who);
+  if (workspace_bytes < 0) return fail(V41_EINVAL, "%s: workspace_bytes < 0", who);
+  return V41_OK;
+}
+
+}  // namespace
+
+int64_t v41_linear_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t groups) {
+  if (M <= 0 || N <= 0 || K <= 0 || groups <= 0) return 0;
+  return v41::gemm_workspace_bytes(M, N, K, groups);
+}
+
+int v41_linear_bf16(const v41_bf16* a, int64_t lda, int64_t a_gs, const v41_bf16* w,
+                    int64_t ldw, int64_t w_gs, v41_bf16* y, int64_t ldy, int64_t y_gs, int32_t M,
+                    int32_t N, int32_t K, int32_t groups, void* workspace,
+                    int64_t workspace_bytes, v41_stream stream) {
+  int rc = check_linear("linear_bf16", a, lda, a_gs, w, ldw, w_gs, y, ldy, y_gs, M, N, K, groups,
+                        workspace, workspace_bytes);
+  if (rc) return rc;
+  rc = check_device();
+  if (rc) return rc;
+  v41::LinearArgs la{a, lda, a_gs, w, ldw, w_gs, y, ldy, y_gs, M, N, K, groups, workspace,
+                     workspace ? workspace_bytes : 0};
+  return launched(v41::launch_linear_bf16(la, (hipStream_t)stream), "linear_bf16");
+}
+
+int64_t v41_grouped_output_workspace_bytes(int64_t n_tokens, int32_t n_heads, int32_t head_dim,
+                                           int32_t groups, int32_t rank, int32_t dim) {
+  if (n_tokens <= 0 || n_tokens > 0x7FFFFFFF || groups <= 0 || n_heads % groups != 0)
+    return 0;
+  const int32_t gw = n_heads / groups * head_dim;
+  const int64_t w1 = v41::gemm_workspace_bytes((int32_t)n_tokens, rank, gw, groups);
+  const int64_t w2 = v41::gemm_workspace_bytes((int32_t)n_tokens, dim, groups * rank, 1);
+  return w1 > w2 ? w1 : w2;
+}
+
+int v41_grouped_output(const v41_bf16* o_bar, int64_t n_tokens, int32_t n_heads,
+                       int32_t head_dim, int32_t groups, int32_t rank, int32_t dim,
+                       const v41_bf16* wo_a, const v41_bf16* wo_b, v41_bf16* og, v41_bf16* x,
+                       void* workspace, int64_t workspace_bytes, v41_stream stream) {
+  const char* who = "grouped_output";
+  if (n_tokens < 0 || n_tokens > 0x7FFFFFFF) return fail(V41_EINVAL, "%s: n_tokens out of range", who);
+  if (groups < 1 || n_heads < 1 || n_heads % groups != 0)
+    return fail(V41_EINVAL, "%s: n_heads must be a positive multiple of groups", who);
+  if (head_dim < 1 || rank < 1 || dim < 1)
+    return fail(V41_EINVAL, "%s: head_dim, rank and dim must be positive", who);
+  const int64_t gw = (int64_t)n_heads / groups * head_dim;
+  const int64_t og_w = (int64_t)groups * rank;
+  if (gw > 0x7FFFFFFF || og_w > 0x7FFFFFFF)
+    return fail(V41_EINVAL, "%s: sizes out of range", who);
+  const int32_t M = (int32_t)n_tokens;
+  int rc = check_linear(who, o_bar, groups * gw, gw, wo_a, gw, (int64_t)rank * gw, og, og_w, rank,
+                        M, rank, (int32_t)gw, groups, workspace, workspace_bytes);
+  if (rc) return rc;
+  rc = check_linear(who, og, og_w, 0, wo_b, og_w, 0, x, dim, 0, M, dim, (int32_t)og_w, 1,
+                    workspace, workspace_bytes);
+  if (rc) return rc;
+  if (!aligned16(og)) return fail(V41_EINVAL, "%s: og must be 16-byte aligned", who);
+  rc = check_device();
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t wb = workspace ? workspace_bytes : 0;
+  // o^g_{t, g} = O_bar_{t, heads of g} . W_OA,g^T (block diagonal over groups)
+  v41::LinearArgs l1{o_bar, groups * gw, gw, wo_a, gw, (int64_t)rank * gw, og, og_w, rank, M,
+                     rank, (int32_t)gw, groups, workspace, wb};
+  rc = launched(v41::launch_linear_bf16(l1, s), "grouped_output wo_a");
+  if (rc) return rc;
+  // Delta_t = o^g_t . W_OB^T
+  v41::LinearArgs l2{og, og_w, 0, wo_b, og_w, 0, x, dim, 0, M, dim, (int32_t)og_w, 1, workspace,
+                     wb};
+  return launched(v41::launch_linear_bf16(l2, s), "grouped_output wo_b");
 }
 
 int v41_decode_step(const v41_decode_step_args* a, v41_stream stream) {

@@ -18,7 +18,9 @@ V41_OK, V41_EINVAL, V41_EHIP, V41_EDEVICE = 0, -1, -2, -3
 EXPORTS = ("v41_last_error", "v41_abi_version", "v41_fp8_round_rows", "v41_window_idx",
            "v41_indexer_scores", "v41_topk_select", "v41_sparse_attn_sink",
            "v41_sparse_attn_workspace_bytes", "v41_rope_table", "v41_rope_rows",
-           "v41_rope_fp8_rows", "v41_decode_step", "v41_candidate_blocks")
+           "v41_rope_fp8_rows", "v41_decode_step", "v41_candidate_blocks", "v41_linear_bf16",
+           "v41_linear_workspace_bytes", "v41_grouped_output",
+           "v41_grouped_output_workspace_bytes")
 
 
 class DecodeStepArgs(C.Structure):
@@ -96,6 +98,16 @@ def load() -> C.CDLL:
                                     vp, i32, i64, vp]
     L.v41_candidate_blocks.restype = C.c_int
     L.v41_candidate_blocks.argtypes = [vp, i64, i64, i64, i32, i32, vp, i64, vp]
+    L.v41_linear_bf16.restype = C.c_int
+    L.v41_linear_bf16.argtypes = [vp, i64, i64, vp, i64, i64, vp, i64, i64, i32, i32, i32, i32,
+                                  vp, i64, vp]
+    L.v41_linear_workspace_bytes.restype = C.c_int64
+    L.v41_linear_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.v41_grouped_output.restype = C.c_int
+    L.v41_grouped_output.argtypes = [vp, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i64,
+                                     vp]
+    L.v41_grouped_output_workspace_bytes.restype = C.c_int64
+    L.v41_grouped_output_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i32]
     L.v41_decode_step.restype = C.c_int
     L.v41_decode_step.argtypes = [C.POINTER(DecodeStepArgs), vp]
     _lib = L
@@ -205,3 +217,26 @@ def v41_candidate_blocks(scores, n_sel_rows, n_cols, scores_ld, cand_block, topk
                          cand_ld, stream=None) -> None:
     _check(load().v41_candidate_blocks(_ptr(scores), n_sel_rows, n_cols, scores_ld, cand_block,
                                        topk_blocks, _ptr(cand), cand_ld, _stream(stream)))
+
+
+def v41_linear_bf16(a, lda, a_gs, w, ldw, w_gs, y, ldy, y_gs, M, N, K, groups, workspace=None,
+                    workspace_bytes=0, stream=None) -> None:
+    _check(load().v41_linear_bf16(_ptr(a), lda, a_gs, _ptr(w), ldw, w_gs, _ptr(y), ldy, y_gs, M,
+                                  N, K, groups, _ptr(workspace), workspace_bytes,
+                                  _stream(stream)))
+
+
+def v41_linear_workspace_bytes(M, N, K, groups) -> int:
+    return int(load().v41_linear_workspace_bytes(M, N, K, groups))
+
+
+def v41_grouped_output(o_bar, n_tokens, n_heads, head_dim, groups, rank, dim, wo_a, wo_b, og, x,
+                       workspace=None, workspace_bytes=0, stream=None) -> None:
+    _check(load().v41_grouped_output(_ptr(o_bar), n_tokens, n_heads, head_dim, groups, rank, dim,
+                                     _ptr(wo_a), _ptr(wo_b), _ptr(og), _ptr(x), _ptr(workspace),
+                                     workspace_bytes, _stream(stream)))
+
+
+def v41_grouped_output_workspace_bytes(n_tokens, n_heads, head_dim, groups, rank, dim) -> int:
+    return int(load().v41_grouped_output_workspace_bytes(n_tokens, n_heads, head_dim, groups,
+                                                         rank, dim))

@@ -65,6 +65,8 @@ def lib():
         L.ora_grouped_output.argtypes = [u16p, u16p, u16p, C.c_int64, C.c_int32, C.c_int32,
                                          C.c_int32, C.c_int32, u16p, u16p]
         L.ora_grouped_output.restype = None
+        L.ora_linear_bf16.argtypes = [u16p, u16p, C.c_int64, C.c_int32, C.c_int32, u16p]
+        L.ora_linear_bf16.restype = None
         _lib = L
     return _lib
 
@@ -332,3 +334,16 @@ def grouped_output(o_bar: np.ndarray, wo_a: np.ndarray, wo_b: np.ndarray, groups
                              groups, gr // groups, gw, wb.shape[0], _p(og, C.c_uint16),
                              _p(x, C.c_uint16))
     return og, x
+
+
+def linear_bf16(a: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """a [M, K], w [N, K] bf16 -> y [M, N] bf16: double sums rounded once."""
+    a = _c(a, np.uint16)
+    w = _c(w, np.uint16)
+    M, K = a.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("a and w disagree on K")
+    y = np.empty((M, N), dtype=np.uint16)
+    lib().ora_linear_bf16(_p(a, C.c_uint16), _p(w, C.c_uint16), M, N, K, _p(y, C.c_uint16))
+    return y

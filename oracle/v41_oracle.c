@@ -642,3 +642,22 @@ void ora_grouped_output(const uint16_t *o_bar, const uint16_t *wo_a,
         }
     }
 }
+
+/*
+ * One projection as the pages' linear_bf16 ("deepseek_v41_ref::attn"
+ * precision paragraph: f32 accumulation, bf16 result; weights [out, in]):
+ * y[m][n] = sum_k a[m][k] * w[n][k], the sum in double, rounded once to bf16.
+ * a: [M][K], w: [N][K], y: [M][N], all bf16.
+ */
+void ora_linear_bf16(const uint16_t *a, const uint16_t *w, int64_t M,
+                     int32_t N, int32_t K, uint16_t *y)
+{
+    for (int64_t m = 0; m < M; ++m)
+        for (int32_t n = 0; n < N; ++n) {
+            double acc = 0.0;
+            for (int32_t k = 0; k < K; ++k)
+                acc += ora_bf16_to_double(a[m * K + k]) *
+                       ora_bf16_to_double(w[(int64_t)n * K + k]);
+            y[m * N + n] = ora_double_to_bf16(acc);
+        }
+}

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib.v41_abi_version() == 4
+    assert lib.v41_abi_version() == 5
 
 
 def _err(lib):
@@ -210,3 +210,21 @@ def test_candidate_blocks_rejects_bad_arguments(lib):
     assert "cand_ld" in _err(lib)
     assert lib.v41_candidate_blocks(1024, 1, 1 << 20, 1 << 20, 8, 4, 4096, 1 << 17,
                                     None) == -1 and "exceed" in _err(lib)
+
+
+def test_linear_rejects_bad_arguments(lib):
+    assert lib.v41_linear_bf16(1024, 96, 0, 4096, 96, 0, 8192, 8, 0, 4, 8, 96, 1, None, 0,
+                               None) == -1 and "multiple of 64" in _err(lib)
+    assert lib.v41_linear_bf16(1024, 60, 0, 4096, 64, 0, 8192, 8, 0, 4, 8, 64, 1, None, 0,
+                               None) == -1 and "lda" in _err(lib)
+    assert lib.v41_linear_bf16(1028, 64, 0, 4096, 64, 0, 8192, 8, 0, 4, 8, 64, 1, None, 0,
+                               None) == -1 and "aligned" in _err(lib)
+    assert lib.v41_grouped_output(1024, 4, 6, 64, 4, 64, 64, 4096, 8192, 16384, 32768, None, 0,
+                                  None) == -1 and "multiple of groups" in _err(lib)
+
+
+def test_workspace_queries_for_projections(lib):
+    # decode sizes split K (f32 partials per split); prefill sizes do not
+    assert lib.v41_linear_workspace_bytes(64, 5120, 8192, 1) > 0
+    assert lib.v41_linear_workspace_bytes(2048, 5120, 8192, 1) == 0
+    assert lib.v41_grouped_output_workspace_bytes(64, 64, 512, 8, 1024, 5120) > 0

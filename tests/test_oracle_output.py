@@ -90,3 +90,29 @@ def test_rejects_mismatched_shapes():
     with pytest.raises(ValueError):
         O.grouped_output(np.zeros((1, 10), np.uint16), np.zeros((4, 4), np.uint16),
                          np.zeros((2, 4), np.uint16), 2)
+
+
+def test_linear_is_a_matrix_product():
+    a = S.normal_bf16(11, S.TAG_Q, (7, 160))
+    w = S.normal_bf16(12, S.TAG_MISC, (33, 160))
+    y = O.linear_bf16(a, w)
+    exact = f64(a) @ f64(w).T
+    assert np.all(np.abs(f64(y) - exact) <= 0.5 * ulp_bf16(exact))
+    # a hand case: [out, in] weights
+    a = bf([[1, 2, 3]])
+    w = bf([[1, 0, 0], [0, 1, 1], [2, -1, 4]])
+    assert f64(O.linear_bf16(a, w))[0].tolist() == [1.0, 5.0, 12.0]
+
+
+def test_grouped_output_is_two_linear_projections():
+    """Each group's block is a linear_bf16 of its slice, and x is a
+    linear_bf16 of the bf16 og (the same rounding points)."""
+    T, G, gw, R, dim = 4, 3, 64, 16, 24
+    o = S.normal_bf16(13, S.TAG_Q, (T, G * gw))
+    wa = S.normal_bf16(14, S.TAG_MISC, (G * R, gw))
+    wb = S.normal_bf16(15, S.TAG_MISC, (dim, G * R))
+    og, x = O.grouped_output(o, wa, wb, G)
+    for g in range(G):
+        assert np.array_equal(og[:, g * R:(g + 1) * R],
+                              O.linear_bf16(o[:, g * gw:(g + 1) * gw], wa[g * R:(g + 1) * R]))
+    assert np.array_equal(x, O.linear_bf16(og, wb))
