@@ -285,6 +285,44 @@ def time_candidate_blocks(torch, device, steps):
             "achieved_GBs": round(nbytes / (us * 1e-6) / 1e9, 1)}
 
 
+def time_grouped_output(torch, device, steps, n_tokens):
+    """The output side of a step: the inverse rotation of o's tails, then
+    wo_a (8 groups, rank 1024, 4096 features each) and wo_b (5120 x 8192),
+    synthetic N(0, 1/fan_in) bf16 weights.  Per-step us, the weight stream
+    (decode) and the MFMA rate (prefill) of the projections."""
+    from inputs import synth
+    from indexer_top_sink_amd import layer as LY
+    from indexer_top_sink_amd import v41
+    T, H, D, G, R, dim, rd = n_tokens, 64, 512, 8, 1024, 5120, 64
+    gw = H * D // G
+
+    def weights(seed, shape, fan_in):
+        x = synth.normal_f32(seed, synth.TAG_MISC, shape) * (1.0 / fan_in ** 0.5)
+        return LY.to_device_bf16(synth.f32_to_bf16_bits(x), device)
+
+    wa, wb = weights(0x5EED5001, (G * R, gw), gw), weights(0x5EED5002, (dim, G * R), G * R)
+    o = LY.to_device_bf16(synth.normal_bf16(0x5EED5003, synth.TAG_Q, (T, H, D)), device)
+    pos = 32767 if T <= 64 else 0
+    rt = LY.rope_table(10000.0, rd, pos + T, device)
+    og = torch.empty(T, G * R, dtype=torch.bfloat16, device=device)
+    x = torch.empty(T, dim, dtype=torch.bfloat16, device=device)
+    wsb = v41.v41_grouped_output_workspace_bytes(T, H, D, G, R, dim)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=device)
+    inv = lambda: v41.v41_rope_rows(o, D, o, D, 1 if T > 64 else T, T if T > 64 else 1, H, D,
+                                    rd, rt.table, rt.n_pos, None, pos, 1)
+    proj = lambda: v41.v41_grouped_output(o, T, H, D, G, R, dim, wa, wb, og, x, ws, wsb)
+    reps = max(4, steps // 4)
+    g_all = capture([inv, proj] * 4, torch)
+    us_all = time_replays([g_all], reps, torch) * 1e3 / 4
+    g_proj = capture([proj] * 4, torch)
+    us_proj = time_replays([g_proj], reps, torch) * 1e3 / 4
+    wbytes = (G * R * gw + dim * G * R) * 2
+    flops = 2 * T * (G * R * gw + dim * G * R)
+    return {"tokens": T, "us_per_step": round(us_all, 2), "projections_us": round(us_proj, 2),
+            "weight_bytes": wbytes, "weights_GBs": round(wbytes / (us_proj * 1e-6) / 1e9, 1),
+            "flops": flops, "TFLOPs": round(flops / (us_proj * 1e-6) / 1e12, 1)}
+
+
 # ----------------------------------------------------------------- CPU baseline
 def cpu_baseline(wl, n_sample, budget_s=30.0):
     """The oracle (plain C, one thread) on the first sequences / tokens of the
@@ -560,8 +598,11 @@ def main():
             "us_per_step_separate_calls": round(lsep * 1e3, 2) if lsep is not None else None,
             "kernels_us": {k: round(v, 2) for k, v in lk.items()}}
     if not args.no_secondary:
-        out.setdefault("secondary", {})["candidate_blocks"] = time_candidate_blocks(
-            torch, device, args.steps)
+        sec = out.setdefault("secondary", {})
+        sec["candidate_blocks"] = time_candidate_blocks(torch, device, args.steps)
+        sec["grouped_output"] = {
+            "decode64": time_grouped_output(torch, device, args.steps, 64),
+            "prefill": time_grouped_output(torch, device, args.steps, 2048)}
     if not args.no_secondary and not args.rope:
         # the same step with the rotary epilogue in front (pre-rotation q and kv)
         rw, rms, rk, rwork, rsep = run_workload(wl.name, args.steps, args.warmup,
