@@ -172,6 +172,43 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_kernel(GemmParams p) {
 }
 
 // y = bf16(sum over splits of the partials), splits added in index order.
+// One thread per 4 consecutive outputs of a row (N a multiple of 4): 16-byte
+// partial loads, all splits issued before the adds, one 8-byte store.
+__global__ __launch_bounds__(256) void gemm_reduce4_kernel(const float* __restrict__ part,
+                                                           int32_t splits, int32_t rows,
+                                                           int32_t M, int32_t N, uint16_t* y,
+                                                           int64_t ldy, int64_t y_gs) {
+  const int32_t q = N / 4;  // quads per row
+  const int64_t per_split = (int64_t)rows * N;
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // quad index
+  if (e >= (int64_t)rows * q) return;
+  const int64_t row = e / q;                 // g * M + m
+  const int32_t n = (int32_t)(e - row * q) * 4;
+  const float* src = part + row * N + n;
+  f32x4 acc = *reinterpret_cast<const f32x4*>(src);
+  for (int32_t k = 1; k < splits; ++k) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(src + k * per_split);
+    acc[0] += v[0];
+    acc[1] += v[1];
+    acc[2] += v[2];
+    acc[3] += v[3];
+  }
+  const int64_t g = row / M, m = row - g * M;
+  uint2 o;
+  o.x = f32_to_bf16_bits(acc[0]) | (f32_to_bf16_bits(acc[1]) << 16);
+  o.y = f32_to_bf16_bits(acc[2]) | (f32_to_bf16_bits(acc[3]) << 16);
+  uint16_t* dst = y + g * y_gs + m * ldy + n;
+  if ((reinterpret_cast<uintptr_t>(dst) & 7u) == 0) {
+    *reinterpret_cast<uint2*>(dst) = o;
+  } else {
+    dst[0] = (uint16_t)(o.x & 0xFFFFu);
+    dst[1] = (uint16_t)(o.x >> 16);
+    dst[2] = (uint16_t)(o.y & 0xFFFFu);
+    dst[3] = (uint16_t)(o.y >> 16);
+  }
+}
+
+// The same for any N, one output per thread.
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restrict__ part,
                                                           int32_t splits, int32_t groups,
                                                           int32_t M, int32_t N, uint16_t* y,
@@ -247,10 +284,16 @@ hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   const int64_t n = (int64_t)p.groups * p.M * p.N;
-  int64_t blocks = (n + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p.part,
-                     p.splits, p.groups, p.M, p.N, a.y, a.ldy, a.y_gs);
+  if (p.N % 4 == 0 && n / 4 <= 0x7FFFFFFFLL * 256) {
+    const int64_t blocks = (n / 4 + 255) / 256;
+    hipLaunchKernelGGL(gemm_reduce4_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p.part,
+                       p.splits, p.groups * p.M, p.M, p.N, a.y, a.ldy, a.y_gs);
+  } else {
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(gemm_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p.part,
+                       p.splits, p.groups, p.M, p.N, a.y, a.ldy, a.y_gs);
+  }
   return hipGetLastError();
 }
 

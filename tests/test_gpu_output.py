@@ -70,6 +70,7 @@ def weights(seed, shape, fan_in):
     (17, 72, 128, 3, None),       # ragged, grouped, small-tile path
     (2048, 512, 1024, 1, 24),     # many rows
     (1, 64, 64, 1, None),
+    (5, 70, 2048, 2, None),       # split K with N not a multiple of 4
 ])
 def test_linear_parity(v41, M, N, K, G, sample):
     say("linear", M, N, K, G)
