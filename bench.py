@@ -513,6 +513,9 @@ def main():
     ap.add_argument("--separate-calls", action="store_true",
                     help="time a decode step as the separate calls instead of one "
                          "v41_decode_step call")
+    ap.add_argument("--output-side", action="store_true",
+                    help="time only the output side (inverse rotation, wo_a, wo_b) at decode64 "
+                         "and prefill sizes and print that as the JSON line")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0)
@@ -541,6 +544,14 @@ def main():
         log(f"copy calibration: {n} bytes read and {n} written per copy")
         del src, dst
 
+    if args.output_side:
+        res = {"decode64": time_grouped_output(torch, device, args.steps, 64),
+               "prefill": time_grouped_output(torch, device, args.steps, 2048)}
+        print(json.dumps({"metric": "output side us per step (inverse rotation, wo_a, wo_b)",
+                          "value": res["decode64"]["us_per_step"], "unit": "us",
+                          "higher_is_better": False, "data": "synthetic", "detail": res}),
+              flush=True)
+        return
     wl, ms_step, kern_us, work, ms_sep = run_workload(args.workload, args.steps, args.warmup,
                                                       args.input_sets, torch, device,
                                                       rope=args.rope,
