@@ -363,15 +363,15 @@ int64_t v41_grouped_output_workspace_bytes(int64_t n_tokens, int32_t n_heads,
  * mod window on the device, and the per-step index buffers are rebuilt on the
  * device instead of being uploaded).  The step is the same computation as the
  * separate calls, in fewer launches:
- *   1. one launch: when rope_dim > 0, the q tails rotated in place
+ *   1. the front work: when rope_dim > 0, the q tails rotated in place
  *      (v41_rope_rows) and the new kv rows rotated; the kv rows through the
  *      fp8 round trip into ring slot pos[b] mod window (v41_fp8_round_rows /
  *      v41_rope_fp8_rows); the window indices of the whole ring, oldest first
  *      (v41_window_idx at a decode);
  *   2. when ratio >= 1: the indexer scores with n(b) =
- *      min(n_rows, floor((pos[b] + 1) / ratio)) (v41_indexer_scores), then
- *      the top-k written after the window columns, offset by window
- *      (v41_topk_select);
+ *      min(n_rows, floor((pos[b] + 1) / ratio)) (v41_indexer_scores), in the
+ *      same launch as the front work; then the top-k written after the window
+ *      columns, offset by window (v41_topk_select);
  *   3. the sparse attention with the sink over [ring ; latent rows]
  *      (v41_sparse_attn_sink).
  * Sequences may sit at different positions.  A sequence whose pos[b] is

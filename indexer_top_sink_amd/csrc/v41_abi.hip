@@ -13,6 +13,7 @@
 #include "v41_common.h"
 #include "v41_rope.h"
 #include "v41_gemm.h"
+#include "v41_front.h"
 
 namespace {
 
@@ -551,20 +552,24 @@ int v41_decode_step(const v41_decode_step_args* a, v41_stream stream) {
   f.row_len = D;
   f.window = a->window;
   f.rope_dim = a->rope_dim;
-  rc = launched(v41::launch_decode_front(f, s), "decode_step front");
-  if (rc) return rc;
   const int64_t n_rows = compressed ? a->n_rows : 0;
   if (compressed) {
-    // start_pos 1 only marks the decode form; the positions come from pos
-    rc = launched(v41::launch_indexer_scores(a->qI, a->kI, a->kI_bs, a->w, nullptr, 0, 1,
-                                             a->batch, 1, 1, a->pos, a->ratio, a->index_heads,
-                                             a->index_dim, n_rows, a->scores, n_rows, s),
-                  "decode_step indexer");
+    // the indexer scores with the front work as extra workgroups of the same
+    // launch (the two touch disjoint buffers); start_pos 1 only marks the
+    // decode form, the positions come from pos
+    rc = launched(v41::launch_indexer_scores_front(a->qI, a->kI, a->kI_bs, a->w, nullptr, 0, 1,
+                                                   a->batch, 1, 1, a->pos, a->ratio,
+                                                   a->index_heads, a->index_dim, n_rows,
+                                                   a->scores, n_rows, &f, s),
+                  "decode_step front + indexer");
     if (rc) return rc;
     // with no compressed rows the top-k reads nothing and writes k absent entries
     rc = launched(v41::launch_topk_select(a->scores, a->batch, n_rows, n_rows, topk, a->window,
                                           a->idx + a->window, width, s),
                   "decode_step top-k");
+    if (rc) return rc;
+  } else {
+    rc = launched(v41::launch_decode_front(f, s), "decode_step front");
     if (rc) return rc;
   }
   v41::AttnArgs t;

@@ -24,6 +24,7 @@
 // a last pass overwrites the masked positions with -inf (their products were
 // computed and are discarded).
 #include "v41_common.h"
+#include "v41_front.h"
 
 namespace v41 {
 namespace {
@@ -115,7 +116,12 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(
     const float* __restrict__ w, const uint8_t* __restrict__ cand, int32_t cand_width,
     int32_t cand_block, int32_t n_tokens, int64_t start_pos, const int32_t* __restrict__ pos,
     int32_t ratio, int32_t n_heads, int32_t n_rows, float* __restrict__ scores,
-    int64_t scores_ld, int32_t blocks_per_query) {
+    int64_t scores_ld, int32_t blocks_per_query, FrontParams front, int32_t score_blocks) {
+  // workgroups past the score grid carry a decode step's front work
+  if ((int32_t)blockIdx.x >= score_blocks) {
+    decode_front_block(front, (int32_t)blockIdx.x - score_blocks);
+    return;
+  }
   using KT = KeyTile<DI>;
   constexpr int KS = KT::KS;
   constexpr int kQBytes = 16 * HT * DI * 2;
@@ -246,11 +252,12 @@ hipError_t dispatch_heads(int ht, dim3 grid, hipStream_t s, const uint16_t* qI,
                           const uint8_t* cand, int32_t cand_width, int32_t cand_block,
                           int32_t n_tokens, int64_t start_pos, const int32_t* pos,
                           int32_t ratio, int32_t n_heads, int32_t n_rows, float* scores,
-                          int64_t scores_ld, int32_t bpq) {
+                          int64_t scores_ld, int32_t bpq, const FrontParams& front,
+                          int32_t score_blocks) {
 #define V41_IDX_LAUNCH(HT_)                                                                   \
   hipLaunchKernelGGL((indexer_kernel<DI, HT_, NT>), grid, dim3(kThreads), 0, s, qI, kI,      \
                      kI_bs, w, cand, cand_width, cand_block, n_tokens, start_pos, pos,       \
-                     ratio, n_heads, n_rows, scores, scores_ld, bpq)
+                     ratio, n_heads, n_rows, scores, scores_ld, bpq, front, score_blocks)
   switch (ht) {
     case 1: V41_IDX_LAUNCH(1); break;
     case 2: V41_IDX_LAUNCH(2); break;
@@ -266,26 +273,35 @@ hipError_t dispatch_nt(bool nt, int ht, dim3 grid, hipStream_t s, const uint16_t
                        const uint16_t* kI, int64_t kI_bs, const float* w, const uint8_t* cand,
                        int32_t cand_width, int32_t cand_block, int32_t n_tokens,
                        int64_t start_pos, const int32_t* pos, int32_t ratio, int32_t n_heads,
-                       int32_t n_rows, float* scores, int64_t scores_ld, int32_t bpq) {
+                       int32_t n_rows, float* scores, int64_t scores_ld, int32_t bpq,
+                       const FrontParams& front, int32_t score_blocks) {
   if (nt)
     return dispatch_heads<DI, 1>(ht, grid, s, qI, kI, kI_bs, w, cand, cand_width, cand_block,
                                  n_tokens, start_pos, pos, ratio, n_heads, n_rows, scores,
-                                 scores_ld, bpq);
+                                 scores_ld, bpq, front, score_blocks);
   return dispatch_heads<DI, 0>(ht, grid, s, qI, kI, kI_bs, w, cand, cand_width, cand_block,
                                n_tokens, start_pos, pos, ratio, n_heads, n_rows, scores,
-                               scores_ld, bpq);
+                               scores_ld, bpq, front, score_blocks);
 }
 
 }  // namespace
 
-hipError_t launch_indexer_scores(const uint16_t* qI, const uint16_t* kI, int64_t kI_bs,
-                                 const float* w, const uint8_t* cand, int32_t cand_width,
-                                 int32_t cand_block, int32_t batch, int32_t n_tokens,
-                                 int64_t start_pos, const int32_t* pos, int32_t ratio,
-                                 int32_t n_heads, int32_t head_dim, int64_t n_rows,
-                                 float* scores, int64_t scores_ld, hipStream_t s) {
+hipError_t launch_indexer_scores_front(const uint16_t* qI, const uint16_t* kI, int64_t kI_bs,
+                                       const float* w, const uint8_t* cand, int32_t cand_width,
+                                       int32_t cand_block, int32_t batch, int32_t n_tokens,
+                                       int64_t start_pos, const int32_t* pos, int32_t ratio,
+                                       int32_t n_heads, int32_t head_dim, int64_t n_rows,
+                                       float* scores, int64_t scores_ld,
+                                       const DecodeFrontArgs* front_args, hipStream_t s) {
   const int64_t nq = (int64_t)batch * n_tokens;
-  if (nq == 0 || n_rows == 0) return hipSuccess;
+  FrontParams front{};
+  const int32_t front_blocks =
+      (front_args != nullptr && front_args->batch > 0) ? make_front_params(*front_args, front) : 0;
+  if (nq == 0 || n_rows == 0) {
+    if (front_blocks == 0) return hipSuccess;
+    // nothing to score: the front work alone
+    return launch_decode_front(*front_args, s);
+  }
   // Workgroups per query: about 384 over the whole grid (1.5 per CU; up to 3
   // fit in LDS), the best measured for decode at 16 and 64 sequences, but at
   // least two 16-key blocks for each wavefront.
@@ -294,8 +310,9 @@ hipError_t launch_indexer_scores(const uint16_t* qI, const uint16_t* kI, int64_t
   const int64_t bpq_max = nbt / (2 * kWaves);
   if (bpq > bpq_max) bpq = bpq_max;
   if (bpq < 1) bpq = 1;
-  if (nq * bpq > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)(nq * bpq));
+  if (nq * bpq + front_blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
+  const int32_t score_blocks = (int32_t)(nq * bpq);
+  const dim3 grid((unsigned)(score_blocks + front_blocks));
   const int ht = (n_heads + 15) / 16;
   // a key serves one query at a decode step: stream it past the caches
   const bool nt = n_tokens == 1;
@@ -304,16 +321,27 @@ hipError_t launch_indexer_scores(const uint16_t* qI, const uint16_t* kI, int64_t
     case 32:
       return dispatch_nt<32>(nt, ht, grid, s, qI, kI, kI_bs, w, cand, cand_width, cand_block,
                              n_tokens, start_pos, pos, ratio, n_heads, rows, scores, scores_ld,
-                             (int32_t)bpq);
+                             (int32_t)bpq, front, score_blocks);
     case 64:
       return dispatch_nt<64>(nt, ht, grid, s, qI, kI, kI_bs, w, cand, cand_width, cand_block,
                              n_tokens, start_pos, pos, ratio, n_heads, rows, scores, scores_ld,
-                             (int32_t)bpq);
+                             (int32_t)bpq, front, score_blocks);
     default:
       return dispatch_nt<128>(nt, ht, grid, s, qI, kI, kI_bs, w, cand, cand_width, cand_block,
                               n_tokens, start_pos, pos, ratio, n_heads, rows, scores, scores_ld,
-                              (int32_t)bpq);
+                              (int32_t)bpq, front, score_blocks);
   }
+}
+
+hipError_t launch_indexer_scores(const uint16_t* qI, const uint16_t* kI, int64_t kI_bs,
+                                 const float* w, const uint8_t* cand, int32_t cand_width,
+                                 int32_t cand_block, int32_t batch, int32_t n_tokens,
+                                 int64_t start_pos, const int32_t* pos, int32_t ratio,
+                                 int32_t n_heads, int32_t head_dim, int64_t n_rows,
+                                 float* scores, int64_t scores_ld, hipStream_t s) {
+  return launch_indexer_scores_front(qI, kI, kI_bs, w, cand, cand_width, cand_block, batch,
+                                     n_tokens, start_pos, pos, ratio, n_heads, head_dim, n_rows,
+                                     scores, scores_ld, nullptr, s);
 }
 
 }  // namespace v41
