@@ -286,10 +286,11 @@ def time_candidate_blocks(torch, device, steps):
 
 
 def time_grouped_output(torch, device, steps, n_tokens):
-    """The output side of a step: the inverse rotation of o's tails, then
-    wo_a (8 groups, rank 1024, 4096 features each) and wo_b (5120 x 8192),
-    synthetic N(0, 1/fan_in) bf16 weights.  Per-step us, the weight stream
-    (decode) and the MFMA rate (prefill) of the projections."""
+    """The output side of a step: the inverse rotation of o's tails (in
+    place), wo_a (8 groups, rank 1024, 4096 features each) and wo_b
+    (5120 x 8192), synthetic N(0, 1/fan_in) bf16 weights.  Per-step us, the
+    projections alone, the weight stream (decode) and the MFMA rate (prefill)
+    of the projections."""
     from inputs import synth
     from indexer_top_sink_amd import layer as LY
     from indexer_top_sink_amd import v41
@@ -308,11 +309,18 @@ def time_grouped_output(torch, device, steps, n_tokens):
     x = torch.empty(T, dim, dtype=torch.bfloat16, device=device)
     wsb = v41.v41_grouped_output_workspace_bytes(T, H, D, G, R, dim)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=device)
-    inv = lambda: v41.v41_rope_rows(o, D, o, D, 1 if T > 64 else T, T if T > 64 else 1, H, D,
-                                    rd, rt.table, rt.n_pos, None, pos, 1)
-    proj = lambda: v41.v41_grouped_output(o, T, H, D, G, R, dim, wa, wb, og, x, ws, wsb)
+    # o before its inverse rotation, which the call applies in place (token t
+    # at position pos + t for a chunk, pos for every decode sequence); o keeps
+    # turning back across replays, which changes no cost
+    posd = torch.full((T,), pos, dtype=torch.int32, device=device)
+    step = lambda: v41.v41_grouped_output(
+        o, T, H, D, G, R, dim, wa, wb, og, x, rope_table=rt.table, rope_rows=rt.n_pos,
+        rope_dim=rd, pos=posd if T <= 64 else None, start_pos=pos, workspace=ws,
+        workspace_bytes=wsb)
+    proj = lambda: v41.v41_grouped_output(o, T, H, D, G, R, dim, wa, wb, og, x, workspace=ws,
+                                          workspace_bytes=wsb)
     reps = max(4, steps // 4)
-    g_all = capture([inv, proj] * 4, torch)
+    g_all = capture([step] * 4, torch)
     us_all = time_replays([g_all], reps, torch) * 1e3 / 4
     g_proj = capture([proj] * 4, torch)
     us_proj = time_replays([g_proj], reps, torch) * 1e3 / 4

@@ -337,9 +337,18 @@ int64_t v41_linear_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t grou
  * gw], wo_b [dim, groups * o_rank]).  Two v41_linear_bf16 launches: the
  * block-diagonal wo_a over the groups of contiguous heads, then wo_b over the
  * bf16 o^g.  O_bar is the attention output after the inverse rotation
- * (v41_rope_rows with inverse = 1).
+ * (CSA: O_bar_{h,t,448:} = R_t^-1 O_{h,t,448:}): with rope_table given, o is
+ * the attention output before it, and its rotated tails are first rotated
+ * back in place (v41_rope_rows with inverse = 1), as the model code does to o;
+ * with rope_table NULL, o is O_bar already and is only read.
  *
- *   o_bar  bf16 [n_tokens][n_heads][head_dim]; gw = n_heads / groups * head_dim
+ *   o      bf16 [n_tokens][n_heads][head_dim]; gw = n_heads / groups * head_dim
+ *   rope_table, rope_rows, rope_dim: the RoPE table (v41_rope_table's layout)
+ *          and the rotated tail of each head (a multiple of 8), or NULL
+ *   pos    device int32 [n_tokens] (token t is a sequence's token at pos[t],
+ *          as at a decode), or NULL: token t at start_pos + t (a chunk; the
+ *          positions must lie in the table); a token whose device position is
+ *          outside the table keeps its tails unrotated
  *   wo_a   bf16 [groups * rank][gw]; wo_b bf16 [dim][groups * rank]
  *   og     bf16 [n_tokens][groups * rank] (written; the input of wo_b)
  *   x      bf16 [n_tokens][dim]
@@ -347,10 +356,12 @@ int64_t v41_linear_workspace_bytes(int32_t M, int32_t N, int32_t K, int32_t grou
  *   workspace: at least v41_grouped_output_workspace_bytes(...) bytes to
  *       split K at decode sizes (optional).
  */
-int v41_grouped_output(const v41_bf16 *o_bar, int64_t n_tokens, int32_t n_heads,
+int v41_grouped_output(v41_bf16 *o, int64_t n_tokens, int32_t n_heads,
                        int32_t head_dim, int32_t groups, int32_t rank, int32_t dim,
                        const v41_bf16 *wo_a, const v41_bf16 *wo_b, v41_bf16 *og, v41_bf16 *x,
-                       void *workspace, int64_t workspace_bytes, v41_stream stream);
+                       const float *rope_table, int64_t rope_rows, int32_t rope_dim,
+                       const int32_t *pos, int64_t start_pos, void *workspace,
+                       int64_t workspace_bytes, v41_stream stream);
 
 int64_t v41_grouped_output_workspace_bytes(int64_t n_tokens, int32_t n_heads,
                                            int32_t head_dim, int32_t groups, int32_t rank,

@@ -65,7 +65,7 @@ extern "C" {
 
 const char* v41_last_error(void) { return g_err; }
 
-int v41_abi_version(void) { return 5; }
+int v41_abi_version(void) { return 6; }
 
 int v41_fp8_round_rows(const v41_bf16* in, int64_t in_ld, v41_bf16* out, int64_t out_ld,
                        int64_t rows, int32_t row_len, v41_bf16* ring, int32_t ring_slots,
@@ -436,11 +436,16 @@ int64_t v41_grouped_output_workspace_bytes(int64_t n_tokens, int32_t n_heads, in
   return w1 > w2 ? w1 : w2;
 }
 
-int v41_grouped_output(const v41_bf16* o_bar, int64_t n_tokens, int32_t n_heads,
+int v41_grouped_output(v41_bf16* o, int64_t n_tokens, int32_t n_heads,
                        int32_t head_dim, int32_t groups, int32_t rank, int32_t dim,
                        const v41_bf16* wo_a, const v41_bf16* wo_b, v41_bf16* og, v41_bf16* x,
-                       void* workspace, int64_t workspace_bytes, v41_stream stream) {
+                       const float* rope_table, int64_t rope_rows, int32_t rope_dim,
+                       const int32_t* pos, int64_t start_pos, void* workspace,
+                       int64_t workspace_bytes, v41_stream stream) {
+  const v41_bf16* o_bar = o;
   const char* who = "grouped_output";
+  if (rope_table != nullptr && (int64_t)n_tokens * n_heads * (head_dim / 8) >= 0x7FFFFFFFLL)
+    return fail(V41_EINVAL, "%s: too many rows to rotate", who);
   if (n_tokens < 0 || n_tokens > 0x7FFFFFFF) return fail(V41_EINVAL, "%s: n_tokens out of range", who);
   if (groups < 1 || n_heads < 1 || n_heads % groups != 0)
     return fail(V41_EINVAL, "%s: n_heads must be a positive multiple of groups", who);
@@ -458,11 +463,30 @@ int v41_grouped_output(const v41_bf16* o_bar, int64_t n_tokens, int32_t n_heads,
                     workspace, workspace_bytes);
   if (rc) return rc;
   if (!aligned16(og)) return fail(V41_EINVAL, "%s: og must be 16-byte aligned", who);
+  if (rope_table != nullptr) {
+    if (rope_dim <= 0 || rope_dim % 8 != 0 || rope_dim > head_dim || head_dim % 8 != 0)
+      return fail(V41_EINVAL, "%s: rope_dim must be a positive multiple of 8 within head_dim",
+                  who);
+    if (rope_rows < 1) return fail(V41_EINVAL, "%s: rope_rows < 1", who);
+    if (!aligned16(rope_table) || !aligned16(pos))
+      return fail(V41_EINVAL, "%s: rope_table and pos must be 16-byte aligned", who);
+    if (pos == nullptr && (start_pos < 0 || start_pos + n_tokens > rope_rows))
+      return fail(V41_EINVAL, "%s: positions outside the rope table", who);
+  }
   rc = check_device();
   if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
   const int64_t wb = workspace ? workspace_bytes : 0;
   // o^g_{t, g} = O_bar_{t, heads of g} . W_OA,g^T (block diagonal over groups)
+  if (rope_table != nullptr && M > 0) {
+    // O_bar_{h,t,tail} = R_t^-1 O_{h,t,tail}, in place on o's rotated tails:
+    // token t is sequence t at pos[t] (decode) or start_pos + t (a chunk)
+    v41::RopeRowsArgs r{o, head_dim, o, head_dim, pos != nullptr ? M : 1,
+                        pos != nullptr ? 1 : M, n_heads, head_dim, rope_dim, rope_table,
+                        rope_rows, pos, start_pos, true, false, nullptr, 0, 0};
+    rc = launched(v41::launch_rope_rows(r, s), "grouped_output inverse rotation");
+    if (rc) return rc;
+  }
   v41::LinearArgs l1{o_bar, groups * gw, gw, wo_a, gw, (int64_t)rank * gw, og, og_w, rank, M,
                      rank, (int32_t)gw, groups, workspace, wb};
   rc = launched(v41::launch_linear_bf16(l1, s), "grouped_output wo_a");

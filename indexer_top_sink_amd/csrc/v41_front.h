@@ -13,10 +13,9 @@ namespace v41 {
 // Four complex pairs (x0 + i x1) times (c + i s), binary32 products and sums
 // each rounded on its own (no contraction into fused multiply-adds), results
 // rounded to bf16.
-__device__ __forceinline__ u32x4 rotate_chunk(u32x4 v, const float* tp, float sgn) {
+// t0, t1: the four (cos, sin) table entries of the pairs.
+__device__ __forceinline__ u32x4 rotate_chunk(u32x4 v, f32x4 t0, f32x4 t1, float sgn) {
 #pragma clang fp contract(off)
-  const f32x4 t0 = *reinterpret_cast<const f32x4*>(tp);
-  const f32x4 t1 = *reinterpret_cast<const f32x4*>(tp + 4);
   const float cs[8] = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
   u32x4 o;
 #pragma unroll
@@ -34,6 +33,12 @@ __device__ __forceinline__ u32x4 rotate_chunk(u32x4 v, const float* tp, float sg
     o[i] = f32_to_bf16_bits(re) | (f32_to_bf16_bits(im) << 16);
   }
   return o;
+}
+
+// The same with the entries read from the table at tp.
+__device__ __forceinline__ u32x4 rotate_chunk(u32x4 v, const float* tp, float sgn) {
+  return rotate_chunk(v, *reinterpret_cast<const f32x4*>(tp),
+                      *reinterpret_cast<const f32x4*>(tp + 4), sgn);
 }
 
 // The front of a decode step in one launch, three kinds of workgroups told

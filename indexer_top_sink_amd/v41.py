@@ -105,7 +105,7 @@ def load() -> C.CDLL:
     L.v41_linear_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.v41_grouped_output.restype = C.c_int
     L.v41_grouped_output.argtypes = [vp, i64, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, i64,
-                                     vp]
+                                     i32, vp, i64, vp, i64, vp]
     L.v41_grouped_output_workspace_bytes.restype = C.c_int64
     L.v41_grouped_output_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i32]
     L.v41_decode_step.restype = C.c_int
@@ -230,10 +230,12 @@ def v41_linear_workspace_bytes(M, N, K, groups) -> int:
     return int(load().v41_linear_workspace_bytes(M, N, K, groups))
 
 
-def v41_grouped_output(o_bar, n_tokens, n_heads, head_dim, groups, rank, dim, wo_a, wo_b, og, x,
+def v41_grouped_output(o, n_tokens, n_heads, head_dim, groups, rank, dim, wo_a, wo_b, og, x,
+                       rope_table=None, rope_rows=0, rope_dim=0, pos=None, start_pos=0,
                        workspace=None, workspace_bytes=0, stream=None) -> None:
-    _check(load().v41_grouped_output(_ptr(o_bar), n_tokens, n_heads, head_dim, groups, rank, dim,
-                                     _ptr(wo_a), _ptr(wo_b), _ptr(og), _ptr(x), _ptr(workspace),
+    _check(load().v41_grouped_output(_ptr(o), n_tokens, n_heads, head_dim, groups, rank, dim,
+                                     _ptr(wo_a), _ptr(wo_b), _ptr(og), _ptr(x), _ptr(rope_table),
+                                     rope_rows, rope_dim, _ptr(pos), start_pos, _ptr(workspace),
                                      workspace_bytes, _stream(stream)))
 
 

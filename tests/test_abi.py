@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib.v41_abi_version() == 5
+    assert lib.v41_abi_version() == 6
 
 
 def _err(lib):
@@ -220,7 +220,11 @@ def test_linear_rejects_bad_arguments(lib):
     assert lib.v41_linear_bf16(1028, 64, 0, 4096, 64, 0, 8192, 8, 0, 4, 8, 64, 1, None, 0,
                                None) == -1 and "aligned" in _err(lib)
     assert lib.v41_grouped_output(1024, 4, 6, 64, 4, 64, 64, 4096, 8192, 16384, 32768, None, 0,
-                                  None) == -1 and "multiple of groups" in _err(lib)
+                                  0, None, 0, None, 0, None) == -1
+    assert "multiple of groups" in _err(lib)
+    # rotation requested with a rope_dim that is not a multiple of 8
+    assert lib.v41_grouped_output(1024, 4, 8, 64, 4, 64, 64, 4096, 8192, 16384, 32768, 65536, 10,
+                                  12, None, 0, None, 0, None) == -1 and "rope_dim" in _err(lib)
 
 
 def test_workspace_queries_for_projections(lib):

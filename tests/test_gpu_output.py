@@ -121,8 +121,22 @@ def test_grouped_output_decode64():
     d_x = torch.empty(T, dim, dtype=torch.int16, device=DEV)
     wsb = v41.v41_grouped_output_workspace_bytes(T, H, D, G, R, dim)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=DEV)
-    v41.v41_grouped_output(d_o, T, H, D, G, R, dim, up16(wa), up16(wb), d_og, d_x, ws, wsb)
+    d_wa, d_wb = up16(wa), up16(wb)
+    v41.v41_grouped_output(d_o, T, H, D, G, R, dim, d_wa, d_wb, d_og, d_x, workspace=ws,
+                           workspace_bytes=wsb)
     og, x = down16(d_og), down16(d_x)
+    # the inverse rotation requested from the call, on the unrotated o: the
+    # same bits as rotating first (positions from a device array)
+    d_o2 = up16(o)
+    d_og2 = torch.empty_like(d_og)
+    d_x2 = torch.empty_like(d_x)
+    pos = torch.full((T,), p, dtype=torch.int32, device=DEV)
+    v41.v41_grouped_output(d_o2, T, H, D, G, R, dim, d_wa, d_wb, d_og2, d_x2, rope_table=rt.table,
+                           rope_rows=rt.n_pos, rope_dim=rd, pos=pos, workspace=ws,
+                           workspace_bytes=wsb)
+    assert np.array_equal(down16(d_og2), og)
+    assert np.array_equal(down16(d_x2), x)
+    assert np.array_equal(down16(d_o2), o_bar)  # o's tails rotated back in place
     rows = [0, 21, 42, 63]
     ob = o_bar.reshape(T, H * D)[rows]
     for g in range(G):
@@ -132,3 +146,39 @@ def test_grouped_output_decode64():
                             f"og group {g}")
     # wo_b on the GPU's own (checked) og
     assert_linear_close(x[rows], O.linear_bf16(og[rows], wb), og[rows], wb, "x")
+
+
+def test_grouped_output_prefill_with_rotation():
+    """2048 tokens at positions 0.., the inverse rotation requested from the
+    call against rotating first; sampled rows against the oracle."""
+    from indexer_top_sink_amd import layer as LY
+    from indexer_top_sink_amd import v41
+    T, H, D, G, R, dim, rd = 2048, 64, 512, 8, 1024, 640, 64
+    gw = H * D // G
+    say("grouped output prefill, with the inverse rotation")
+    o = S.normal_bf16(311, S.TAG_Q, (T, H, D))
+    wa = weights(312, (G * R, gw), gw)
+    wb = weights(313, (dim, G * R), G * R)
+    rt = LY.rope_table(10000.0, rd, T, DEV)
+    d_wa, d_wb = up16(wa), up16(wb)
+    d_og = torch.empty(T, G * R, dtype=torch.int16, device=DEV)
+    d_x = torch.empty(T, dim, dtype=torch.int16, device=DEV)
+    d_o = up16(o)
+    v41.v41_grouped_output(d_o, T, H, D, G, R, dim, d_wa, d_wb, d_og, d_x, rope_table=rt.table,
+                           rope_rows=rt.n_pos, rope_dim=rd, start_pos=0)
+    og, x = down16(d_og), down16(d_x)
+    d_o = up16(o)
+    v41.v41_rope_rows(d_o, D, d_o, D, 1, T, H, D, rd, rt.table, rt.n_pos, None, 0, 1)
+    d_og2 = torch.empty_like(d_og)
+    d_x2 = torch.empty_like(d_x)
+    v41.v41_grouped_output(d_o, T, H, D, G, R, dim, d_wa, d_wb, d_og2, d_x2)
+    assert np.array_equal(down16(d_og2), og)
+    assert np.array_equal(down16(d_x2), x)
+    o_bar = down16(d_o).reshape(T, H * D)
+    rows = [0, 1, 1000, 2047]
+    for g in (0, 5):
+        ag = o_bar[rows][:, g * gw:(g + 1) * gw]
+        wg = wa[g * R:(g + 1) * R]
+        assert_linear_close(og[rows][:, g * R:(g + 1) * R], O.linear_bf16(ag, wg), ag, wg,
+                            f"prefill og group {g}")
+    assert_linear_close(x[rows], O.linear_bf16(og[rows], wb), og[rows], wb, "prefill x")
