@@ -25,6 +25,7 @@
 // The candidate-block selection runs the same select over per-block maxima
 // and writes a byte mask instead of positions.
 #include "v41_common.h"
+#include "v41_wave.h"
 
 namespace v41 {
 namespace {
@@ -49,12 +50,7 @@ struct TopkShared {
 template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, TopkShared<NT>& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const uint32_t o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
+  const uint32_t incl = wave_incl_scan_u32(v);
   if (lane == kWave - 1) sh.red[0][wave] = incl;
   __syncthreads();
   uint32_t base = 0;
@@ -69,12 +65,9 @@ __device__ __forceinline__ void block_stats(uint32_t nv, uint32_t kmin, uint32_t
                                             TopkShared<NT>& sh, uint32_t& o_nv,
                                             uint32_t& o_min, uint32_t& o_max) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    nv += __shfl_xor(nv, off);
-    kmin = min(kmin, (uint32_t)__shfl_xor(kmin, off));
-    kmax = max(kmax, (uint32_t)__shfl_xor(kmax, off));
-  }
+  nv = wave_sum_u32(nv);
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
   if (lane == 0) {
     sh.red[0][wave] = nv;
     sh.red[1][wave] = kmin;
@@ -132,12 +125,7 @@ __device__ __forceinline__ void radix_select(ForKeys for_keys, uint32_t m, uint3
 #pragma unroll
         for (int cp = 0; cp < kHistCopies; ++cp) c[j] += hist[cp * 256 + 255 - 4 * lane - j];
       const uint32_t s = c[0] + c[1] + c[2] + c[3];
-      uint32_t incl = s;
-#pragma unroll
-      for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-      }
+      const uint32_t incl = wave_incl_scan_u32(s);
       const uint32_t excl = incl - s;
       if (excl < need_r && need_r <= incl) {
         uint32_t cum = excl;
