@@ -228,6 +228,25 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // NS: LDS ring depth in tiles (NS - 1 tiles in flight ahead of the one in use).
+// Maximum / sum over the four lanes 16 apart (the k-groups of an MFMA
+// operand), on the permlane swaps.
+__device__ __forceinline__ float group_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
+}
+__device__ __forceinline__ float group_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
+}
+
 template <int D, int NS>
 __global__ __launch_bounds__(kThreads, NS == 2 ? 2 : 1) void attn_kernel(Params p) {
   using TL = Tile<D, kTile>;
@@ -341,8 +360,7 @@ __global__ __launch_bounds__(kThreads, NS == 2 ? 2 : 1) void attn_kernel(Params 
       sv[s] = v;
       mx = fmaxf(mx, v);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = group_max(mx);
     // lazy rescale: the reference moves only when a score exceeds it by more
     // than 2^8 (O and l share the reference, so O / l is unchanged); the
     // branch is uniform across the wavefront
@@ -380,8 +398,7 @@ __global__ __launch_bounds__(kThreads, NS == 2 ? 2 : 1) void attn_kernel(Params 
 
   // ---- epilogue: lane holds O^T[dims 16mt + 4g + i][head r16]
   float l_tot = l_part;
-  l_tot += __shfl_xor(l_tot, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  l_tot = group_sum(l_tot);
   if (!head_ok) return;
   if (p.splits == 1) {
     const float sink_term = (sink2 == kNegInf) ? 0.0f : exp2f(sink2 - m2);
@@ -442,23 +459,6 @@ __device__ __forceinline__ f32x4 mfma16x16x16(u32x2 a, u32x2 b, f32x4 c) {
 }
 
 // v combined (max or sum) over the four 16-lane groups of the wavefront.
-__device__ __forceinline__ float group_max(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  return fmaxf(__uint_as_float(t[0]), __uint_as_float(t[1]));
-}
-__device__ __forceinline__ float group_sum(float v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
-                                                  false);
-  return __uint_as_float(t[0]) + __uint_as_float(t[1]);
-}
-
 // Eight ds_read_b64_tr_b16 at 32-byte steps (eight 16-dim M-tiles of one
 // 16-row K block) and a wait for them.
 __device__ __forceinline__ void tr_load8(u32x2 (&t)[8], uint32_t a) {

@@ -66,8 +66,9 @@ __device__ __forceinline__ u32x4 fp8_round_chunk(u32x4 v, float inv_s, float s) 
 
 // Block amax over the aligned quad of lanes that own one 32-value block.
 __device__ __forceinline__ uint32_t quad_max(uint32_t m) {
-  m = max(m, (uint32_t)__shfl_xor((int)m, 1));
-  m = max(m, (uint32_t)__shfl_xor((int)m, 2));
+  // quad_perm [1,0,3,2] then [2,3,0,1] on the DPP path
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0xB1, 0xF, 0xF, false));
+  m = max(m, (uint32_t)__builtin_amdgcn_update_dpp((int)m, (int)m, 0x4E, 0xF, 0xF, false));
   return m;
 }
 

@@ -228,8 +228,16 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(
         for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
           for (int e = 0; e < 4; ++e) sum += wh[ht][e] * fmaxf(acc[ht][e], 0.0f);
-        sum += __shfl_xor(sum, 16);
-        sum += __shfl_xor(sum, 32);
+        {
+          // the four k-groups' partial sums of the key (lanes 16 and 32
+          // apart), on the permlane swaps
+          const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(sum),
+                                                          __float_as_uint(sum), false, false);
+          sum = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+          const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum),
+                                                          __float_as_uint(sum), false, false);
+          sum = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+        }
         const int j = (part + i * wpq) * 16 + r16;
         if (g == 0 && j < n_rows) srow[j] = j < live_end ? sum : kNegInf;
       }
