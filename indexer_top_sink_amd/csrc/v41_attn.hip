@@ -437,13 +437,17 @@ __global__ __launch_bounds__(kThreads, NS == 2 ? 2 : 1) void attn_kernel(Params 
 // work alone on 16-row tiles handed out by an LDS counter, with their own
 // online softmax, and are merged at the end:
 //  * the 16 heads' queries sit in LDS and feed the QK B operand;
-//  * a lane loads its 16 x 16 bytes of a tile straight into the layout of the
-//    QK A operand, one tile ahead;
+//  * a tile's rows are loaded one tile ahead into registers.  For D = 512 a
+//    load instruction fetches one whole 1 KB row (a lane per 16-byte chunk):
+//    loads laid out as the QK operand (16 rows x 64 bytes per instruction)
+//    were measured 2.3x slower on this gather;
+//  * the rows go to the wavefront's own LDS slot, come back in the QK A
+//    layout (ds_read_b128; for D < 512 they are loaded in that layout and
+//    used from registers) and come back transposed (ds_read_b64_tr_b16) as
+//    the A operand of O^T += G^T P^T, all D dims;
 //  * QK: 16 rows x 16 heads over four independent accumulators; the S
 //    accumulator is laid out as the B operand of a 16x16x16 PV product, so
 //    the bf16 probabilities never leave the lane;
-//  * the rows go to the wavefront's own LDS slot and come back transposed
-//    (ds_read_b64_tr_b16) as the A operand of O^T += G^T P^T, all D dims;
 //  * head maxima and sums across the lane groups use permlane swaps;
 //  * no barrier inside the loop; at the end the eight (max, sum, O) are
 //    merged through LDS, half of the dims at a time.
@@ -513,6 +517,7 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
   constexpr int kHalfDT = DT / 2;
   constexpr int kQStride = 2 * D + 16;  // bytes per head row of the query tile
   static_assert(kW * kHalfDT * kWave * 16 <= kW * WS::kBytes, "merge area");
+  static_assert(D != 512 || KS == kWaveRows, "one register per tile row");
   __shared__ __attribute__((aligned(16))) uint8_t slots[kW * WS::kBytes];
   __shared__ __attribute__((aligned(16))) uint8_t qs[kNarrowHeads * kQStride];
   __shared__ int32_t list[kMaxWidth];
@@ -569,14 +574,27 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
   // repeat the first valid row: finite data, probability 0)
   const uint16_t* a_base = p.rows_a + b * p.a_bs;
   const uint16_t* b_base = p.rows_b + b * p.b_bs;
+  //  D = 512: rb[j] = row j of the tile, lane l holding its chunk l ^ swz(j)
+  //  (the slot position of chunk l); otherwise rb[kk] = chunk 4kk + g of row r16
   auto load = [&](int i, u32x4 (&rb)[KS]) {
     int pos = (t_begin + i) * kWaveRows + r16;
     if ((uint32_t)pos >= n_valid) pos = 0;
-    const int64_t ix = list[pos];
-    const uint16_t* src =
-        ((ix < p.rows_a_len) ? a_base + ix * D : b_base + (ix - p.rows_a_len) * D) + 8 * g;
+    if constexpr (D == 512) {
+      const int32_t my_ix = list[pos];
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) rb[kk] = *reinterpret_cast<const u32x4*>(src + 32 * kk);
+      for (int j = 0; j < kWaveRows; ++j) {
+        const int64_t ix = __builtin_amdgcn_readlane(my_ix, j);
+        const uint16_t* src =
+            (ix < p.rows_a_len) ? a_base + ix * D : b_base + (ix - p.rows_a_len) * D;
+        rb[j] = *reinterpret_cast<const u32x4*>(src + 8 * (lane ^ WS::swz(j)));
+      }
+    } else {
+      const int64_t ix = list[pos];
+      const uint16_t* src =
+          ((ix < p.rows_a_len) ? a_base + ix * D : b_base + (ix - p.rows_a_len) * D) + 8 * g;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) rb[kk] = *reinterpret_cast<const u32x4*>(src + 32 * kk);
+    }
   };
 
   const float sink2 = head_ok ? p.sink[head] * kLog2e : 0.0f;
@@ -605,15 +623,29 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
     f32x4 sa[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) sa[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    if constexpr (D == 512) {
+      // rows to the slot, the next tile's loads out, then QK from the slot
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      const u32x4 qv = *reinterpret_cast<const u32x4*>(q_frag + 64 * kk);
-      sa[kk & 3] = mfma16x16x32(as_bf16x8(rb[kk]), as_bf16x8(qv), sa[kk & 3]);
+      for (int j = 0; j < kWaveRows; ++j)
+        *reinterpret_cast<u32x4*>(slot + j * WS::kStride + 16 * lane) = rb[j];
+      if (nxt < nt) load(nxt, rb);
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const u32x4 qv = *reinterpret_cast<const u32x4*>(q_frag + 64 * kk);
+        const u32x4 av = *reinterpret_cast<const u32x4*>(slot + st_off + 64 * kk);
+        sa[kk & 3] = mfma16x16x32(as_bf16x8(av), as_bf16x8(qv), sa[kk & 3]);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        const u32x4 qv = *reinterpret_cast<const u32x4*>(q_frag + 64 * kk);
+        sa[kk & 3] = mfma16x16x32(as_bf16x8(rb[kk]), as_bf16x8(qv), sa[kk & 3]);
+      }
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) *reinterpret_cast<u32x4*>(slot + st_off + 64 * kk) = rb[kk];
+      if (nxt < nt) load(nxt, rb);
     }
     const f32x4 sacc = (sa[0] + sa[1]) + (sa[2] + sa[3]);
-#pragma unroll
-    for (int kk = 0; kk < KS; ++kk) *reinterpret_cast<u32x4*>(slot + st_off + 64 * kk) = rb[kk];
-    if (nxt < nt) load(nxt, rb);
 
     const int rbase = (t_begin + cur) * kWaveRows + 4 * g;
     float sv[4];
