@@ -520,11 +520,10 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
   static_assert(D != 512 || KS == kWaveRows, "one register per tile row");
   __shared__ __attribute__((aligned(16))) uint8_t slots[kW * WS::kBytes];
   __shared__ __attribute__((aligned(16))) uint8_t qs[kNarrowHeads * kQStride];
-  __shared__ int32_t list[kMaxWidth];
-  __shared__ uint32_t wave_cnt[kW];
+  __shared__ int32_t ixs[kMaxWidth];  // the idx row, entries outside the sources as -1
   __shared__ float xm[kW][kNarrowHeads];
   __shared__ float xl[kW][kNarrowHeads];
-  __shared__ uint32_t tile_ctr;  // next tile to hand out
+  __shared__ uint32_t tile_ctr;  // tiles handed out after each wavefront's first
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -542,45 +541,34 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
   const bool head_ok = head < p.n_heads;
   const int64_t total_rows = p.rows_a_len + p.rows_b_len;
 
-  // ---- the 16 heads' queries into LDS (zero rows past n_heads); the
-  // compaction's barriers publish them and the tile counter
-  if (tid == 0) tile_ctr = 0u;
-  {
-    constexpr int CPR = D / 8;
-    const uint16_t* q0 = p.q + (qi * p.n_heads + hg * kNarrowHeads) * D;
-    for (int e = tid; e < kNarrowHeads * CPR; e += kNarrowThreads) {
-      const int h = e / CPR, c = e % CPR;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (hg * kNarrowHeads + h < p.n_heads) v = *reinterpret_cast<const u32x4*>(q0 + h * D + 8 * c);
-      *reinterpret_cast<u32x4*>(qs + h * kQStride + 16 * c) = v;
-    }
-  }
-  const uint32_t n_valid = compact_idx<kW>(p.idx + qi * p.idx_ld, p.width, total_rows, list,
-                                           wave_cnt, wave, lane);
-  const int n_tiles = (int)((n_valid + kWaveRows - 1) / kWaveRows);
+  // Tiles are 16 consecutive entries of the idx row itself (no compaction):
+  // an entry outside the two sources loads row 0 and gets probability 0.
+  const int n_tiles = total_rows > 0 ? (p.width + kWaveRows - 1) / kWaveRows : 0;
   const int tps = (n_tiles + p.splits - 1) / p.splits;
   const int t_begin = split * tps;
   const int t_end = (t_begin + tps < n_tiles) ? t_begin + tps : n_tiles;
   const int nt = t_end > t_begin ? t_end - t_begin : 0;
-  // tiles go to whichever wavefront asks next (the second wavefront of a
-  // SIMD gets fewer issue slots, so a fixed deal leaves it behind)
+  const int32_t* const irow = p.idx + qi * p.idx_ld;
+  // the next tile goes to whichever wavefront asks first (the second
+  // wavefront of a SIMD gets fewer issue slots, so a fixed deal leaves it
+  // behind); each wavefront's first tile is its own index
   auto grab = [&]() -> int {
     uint32_t t = 0u;
     if (lane == 0) t = atomicAdd(&tile_ctr, 1u);
-    return (int)__builtin_amdgcn_readfirstlane(t);
+    return kW + (int)__builtin_amdgcn_readfirstlane(t);
   };
 
-  // ---- a lane's share of a tile: row r16, chunks 4kk + g (rows past n_valid
-  // repeat the first valid row: finite data, probability 0)
+  // ---- a lane's share of a tile: entry r16 of the tile.  Returns the tile's
+  // 16-bit validity mask (bit r: entry r names a row).
   const uint16_t* a_base = p.rows_a + b * p.a_bs;
   const uint16_t* b_base = p.rows_b + b * p.b_bs;
   //  D = 512: rb[j] = row j of the tile, lane l holding its chunk l ^ swz(j)
   //  (the slot position of chunk l); otherwise rb[kk] = chunk 4kk + g of row r16
-  auto load = [&](int i, u32x4 (&rb)[KS]) {
-    int pos = (t_begin + i) * kWaveRows + r16;
-    if ((uint32_t)pos >= n_valid) pos = 0;
+  auto load = [&](int32_t raw, u32x4 (&rb)[KS]) -> uint32_t {
+    const bool ok = raw >= 0 && (int64_t)raw < total_rows;
+    const uint32_t vm = (uint32_t)__ballot(ok) & 0xFFFFu;
+    const int32_t my_ix = ok ? raw : 0;
     if constexpr (D == 512) {
-      const int32_t my_ix = list[pos];
 #pragma unroll
       for (int j = 0; j < kWaveRows; ++j) {
         const int64_t ix = __builtin_amdgcn_readlane(my_ix, j);
@@ -589,13 +577,60 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
         rb[j] = *reinterpret_cast<const u32x4*>(src + 8 * (lane ^ WS::swz(j)));
       }
     } else {
-      const int64_t ix = list[pos];
+      const int64_t ix = my_ix;
       const uint16_t* src =
           ((ix < p.rows_a_len) ? a_base + ix * D : b_base + (ix - p.rows_a_len) * D) + 8 * g;
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) rb[kk] = *reinterpret_cast<const u32x4*>(src + 32 * kk);
     }
+    return vm;
   };
+  auto entry = [&](int tile) -> int {  // this lane's position in the idx row
+    return (t_begin + tile) * kWaveRows + r16;
+  };
+
+  // ---- prologue: the first tile's entries, the idx row and the 16 heads'
+  // queries (zero rows past n_heads) are all requested before anything waits,
+  // then the first tile's rows go out; one barrier publishes the LDS copies
+  // and the tile counter
+  if (tid == 0) tile_ctr = 0u;
+  int cur = wave;
+  int32_t raw0 = -1;
+  if (cur < nt && entry(cur) < p.width) raw0 = irow[entry(cur)];
+  constexpr int kIxPer = kMaxWidth / kNarrowThreads;
+  int32_t iv[kIxPer];
+#pragma unroll
+  for (int j = 0; j < kIxPer; ++j) {
+    const int i = tid + j * kNarrowThreads;
+    iv[j] = (i < p.width) ? irow[i] : -1;
+  }
+  constexpr int CPR = D / 8;
+  constexpr int kQPer = (kNarrowHeads * CPR + kNarrowThreads - 1) / kNarrowThreads;
+  u32x4 qv[kQPer];
+  const uint16_t* q0 = p.q + (qi * p.n_heads + hg * kNarrowHeads) * D;
+#pragma unroll
+  for (int j = 0; j < kQPer; ++j) {
+    const int e = tid + j * kNarrowThreads;
+    const int h = e / CPR, c = e % CPR;
+    qv[j] = (u32x4){0u, 0u, 0u, 0u};
+    if (e < kNarrowHeads * CPR && hg * kNarrowHeads + h < p.n_heads)
+      qv[j] = *reinterpret_cast<const u32x4*>(q0 + h * D + 8 * c);
+  }
+  u32x4 rb[KS];
+  uint32_t vm_cur = 0u;
+  if (cur < nt) vm_cur = load(raw0, rb);
+#pragma unroll
+  for (int j = 0; j < kQPer; ++j) {
+    const int e = tid + j * kNarrowThreads;
+    const int h = e / CPR, c = e % CPR;
+    if (e < kNarrowHeads * CPR) *reinterpret_cast<u32x4*>(qs + h * kQStride + 16 * c) = qv[j];
+  }
+#pragma unroll
+  for (int j = 0; j < kIxPer; ++j) {
+    const int i = tid + j * kNarrowThreads;
+    if (i < p.width) ixs[i] = (iv[j] >= 0 && (int64_t)iv[j] < total_rows) ? iv[j] : -1;
+  }
+  __syncthreads();
 
   const float sink2 = head_ok ? p.sink[head] * kLog2e : 0.0f;
   const float kNegInf = -__builtin_huge_valf();
@@ -614,11 +649,9 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
   const uint32_t tr_addr = (uint32_t)(size_t)(lds_void*)(size_t)(
       slot + tr_row * WS::kStride + 16 * ((tq >> 1) ^ WS::swz(tr_row)) + 8 * (tq & 1));
 
-  u32x4 rb[KS];
-  int cur = grab();
-  if (cur < nt) load(cur, rb);
   while (cur < nt) {
     const int nxt = grab();
+    uint32_t vm_nxt = 0u;
     // S^T: rows 4g + e of the tile, head r16
     f32x4 sa[4];
 #pragma unroll
@@ -628,7 +661,7 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
 #pragma unroll
       for (int j = 0; j < kWaveRows; ++j)
         *reinterpret_cast<u32x4*>(slot + j * WS::kStride + 16 * lane) = rb[j];
-      if (nxt < nt) load(nxt, rb);
+      if (nxt < nt) vm_nxt = load(entry(nxt) < p.width ? ixs[entry(nxt)] : -1, rb);
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
         const u32x4 qv = *reinterpret_cast<const u32x4*>(q_frag + 64 * kk);
@@ -643,17 +676,16 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
       }
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) *reinterpret_cast<u32x4*>(slot + st_off + 64 * kk) = rb[kk];
-      if (nxt < nt) load(nxt, rb);
+      if (nxt < nt) vm_nxt = load(entry(nxt) < p.width ? ixs[entry(nxt)] : -1, rb);
     }
     const f32x4 sacc = (sa[0] + sa[1]) + (sa[2] + sa[3]);
 
-    const int rbase = (t_begin + cur) * kWaveRows + 4 * g;
     float sv[4];
     float mx = kNegInf;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float v = sacc[e] * p.scale_log2;
-      if ((uint32_t)(rbase + e) >= n_valid) v = kNegInf;
+      if (!((vm_cur >> (4 * g + e)) & 1u)) v = kNegInf;
       sv[e] = v;
       mx = fmaxf(mx, v);
     }
@@ -692,6 +724,7 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
       for (int j = 0; j < DT; ++j) acc_o[j] = mfma16x16x16(t[j], pk, acc_o[j]);
     }
     cur = nxt;
+    vm_cur = vm_nxt;
   }
 
   // ---- merge the wavefronts: M = max m_w, O = sum 2^(m_w - M) O_w,

@@ -31,6 +31,7 @@ namespace v41 {
 namespace {
 
 constexpr int kHistCopies = 8;
+constexpr int kHistStride = 257;
 
 __device__ __forceinline__ uint32_t score_key(float s) {
   uint32_t u = __float_as_uint(s);
@@ -41,7 +42,9 @@ __device__ __forceinline__ uint32_t score_key(float s) {
 
 template <int NT>
 struct TopkShared {
-  uint32_t hist[2][kHistCopies * 256];  // alternate passes; the idle one is cleared
+  // alternate passes (the idle one is cleared); copy c of bin b at
+  // c * kHistStride + b, so the copies of one bin sit in distinct banks
+  uint32_t hist[2][kHistCopies * kHistStride];
   uint32_t red[3][NT / kWave];
   uint32_t digit, above, bin;
 };
@@ -102,19 +105,31 @@ __device__ __forceinline__ void radix_select(ForKeys for_keys, uint32_t m, uint3
   const int top = 31 - __clz(range);
   int shift = top > 7 ? top - 7 : 0;
   uint32_t prefix = 0u, pmask = 0u, need_r = m;
-  for (int i = tid; i < kHistCopies * 256; i += NT) sh.hist[0][i] = 0u;
+  for (int i = tid; i < kHistCopies * kHistStride; i += NT) sh.hist[0][i] = 0u;
   __syncthreads();
   for (int pass = 0;; ++pass) {
     uint32_t* const hist = sh.hist[pass & 1];
     // the other copy was last read before the previous pass's final barrier
-    for (int i = tid; i < kHistCopies * 256; i += NT) sh.hist[(pass + 1) & 1][i] = 0u;
-    uint32_t* const myhist = hist + (lane % kHistCopies) * 256;
+    for (int i = tid; i < kHistCopies * kHistStride; i += NT) sh.hist[(pass + 1) & 1][i] = 0u;
+    uint32_t* const myhist = hist + (lane % kHistCopies) * kHistStride;
+    // a run of equal digits among the thread's keys (its positions are
+    // contiguous, so tied scores form runs) costs one atomic
+    uint32_t run_bin = 0u, run_cnt = 0u;
     for_keys([&](uint32_t key) {
       if (key != 0u) {
         const uint32_t d = key - kmin;
-        if ((d & pmask) == prefix) atomicAdd(&myhist[(d >> shift) & 255u], 1u);
+        if ((d & pmask) == prefix) {
+          const uint32_t bin = (d >> shift) & 255u;
+          if (run_cnt != 0u && bin != run_bin) {
+            atomicAdd(&myhist[run_bin], run_cnt);
+            run_cnt = 0u;
+          }
+          run_bin = bin;
+          ++run_cnt;
+        }
       }
     });
+    if (run_cnt != 0u) atomicAdd(&myhist[run_bin], run_cnt);
     __syncthreads();
     if (tid < kWave) {
       // lane l owns bins 255-4l .. 252-4l (summed over the copies); find the
@@ -123,7 +138,7 @@ __device__ __forceinline__ void radix_select(ForKeys for_keys, uint32_t m, uint3
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int cp = 0; cp < kHistCopies; ++cp) c[j] += hist[cp * 256 + 255 - 4 * lane - j];
+        for (int cp = 0; cp < kHistCopies; ++cp) c[j] += hist[cp * kHistStride + 255 - 4 * lane - j];
       const uint32_t s = c[0] + c[1] + c[2] + c[3];
       const uint32_t incl = wave_incl_scan_u32(s);
       const uint32_t excl = incl - s;
