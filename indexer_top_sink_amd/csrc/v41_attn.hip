@@ -270,16 +270,8 @@ __global__ __launch_bounds__(kThreads, NS == 2 ? 2 : 1) void attn_kernel(Params 
   const bool head_ok = head < p.n_heads;
   const int64_t total_rows = p.rows_a_len + p.rows_b_len;
 
-  const uint32_t n_valid = compact_idx<kThreads / kWave>(p.idx + qi * p.idx_ld, p.width,
-                                                         total_rows, list, wave_cnt, wave, lane);
-  const int n_tiles = (int)((n_valid + kTile - 1) / kTile);
-  const int tps = (n_tiles + p.splits - 1) / p.splits;
-  const int t_begin = split * tps;
-  const int t_end = (t_begin + tps < n_tiles) ? t_begin + tps : n_tiles;
-
-  const uint16_t* a_base = p.rows_a + b * p.a_bs;
-  const uint16_t* b_base = p.rows_b + b * p.b_bs;
   // ---- query fragments (B operand of S^T = G Q^T): head r16, dims 32kk+8g..
+  // requested before the idx row, so the two latencies overlap
   bf16x8 qf[KS];
   {
     const uint16_t* qp = p.q + (qi * p.n_heads + (head_ok ? head : 0)) * D + 8 * g;
@@ -290,6 +282,15 @@ __global__ __launch_bounds__(kThreads, NS == 2 ? 2 : 1) void attn_kernel(Params 
       qf[kk] = as_bf16x8(v);
     }
   }
+  const uint32_t n_valid = compact_idx<kThreads / kWave>(p.idx + qi * p.idx_ld, p.width,
+                                                         total_rows, list, wave_cnt, wave, lane);
+  const int n_tiles = (int)((n_valid + kTile - 1) / kTile);
+  const int tps = (n_tiles + p.splits - 1) / p.splits;
+  const int t_begin = split * tps;
+  const int t_end = (t_begin + tps < n_tiles) ? t_begin + tps : n_tiles;
+
+  const uint16_t* a_base = p.rows_a + b * p.a_bs;
+  const uint16_t* b_base = p.rows_b + b * p.b_bs;
   const float sink2 = head_ok ? p.sink[head] * kLog2e : 0.0f;
   const float kNegInf = -__builtin_huge_valf();
   float m2 = sink2;  // reference max on the log2 scale

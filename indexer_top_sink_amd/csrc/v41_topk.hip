@@ -49,6 +49,9 @@ struct TopkShared {
   uint32_t digit, above, bin;
 };
 
+// Capacity of the sampled select's candidate buffer (keys and positions).
+constexpr int kCandCap = 4096;
+
 // Exclusive scan of one value per thread over the block (two barriers).
 template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, TopkShared<NT>& sh) {
@@ -59,6 +62,25 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, TopkShared<NT>& 
   uint32_t base = 0;
   for (int w = 0; w < wave; ++w) base += sh.red[0][w];
   __syncthreads();
+  return base + incl - v;
+}
+
+// The same, also returning the block total.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan_tot(uint32_t v, TopkShared<NT>& sh,
+                                                        uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_scan_u32(v);
+  if (lane == kWave - 1) sh.red[0][wave] = incl;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+  for (int w = 0; w < NT / kWave; ++w) {
+    const uint32_t c = sh.red[0][w];
+    base += (w < wave) ? c : 0u;
+    tot += c;
+  }
+  __syncthreads();
+  total = tot;
   return base + incl - v;
 }
 
@@ -178,6 +200,9 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(const float* __restrict__ 
                                                       int32_t* __restrict__ idx,
                                                       int64_t idx_ld) {
   __shared__ TopkShared<NT> sh;
+  constexpr int kCandN = KPT >= 32 ? kCandCap : 1;  // only long rows sample
+  __shared__ uint32_t cand_key[kCandN];
+  __shared__ int32_t cand_pos[kCandN];
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
   const float* __restrict__ srow = scores + row * scores_ld;
@@ -215,12 +240,94 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(const float* __restrict__ 
 
   uint32_t T = 0u, need = 0u;
   if (nv > (uint32_t)k) {
-    radix_select<NT>(
-        [&](auto f) {
+    // Sampled threshold (rows of 32 keys per thread): a radix select
+    // over one key per thread picks T0, a key that about r * nv / n_s keys
+    // reach, with r set a few standard deviations above the m * n_s / nv
+    // samples expected among the top m.  With G keys above T0 and E equal:
+    //  - G <= m <= G + E: T0 is the m-th key itself (selection: the G keys
+    //    above it and the first m - G equal ones), no further pass;
+    //  - G > m (and G fits the candidate buffer): the top m lie among the G
+    //    keys above T0, which are compacted in position order and selected
+    //    exactly;
+    //  - otherwise the full select below.
+    bool done = false;
+    if constexpr (KPT >= 32) {
+      uint32_t n_s = 0;
+      (void)block_excl_scan_tot<NT>(key[0] != 0u ? 1u : 0u, sh, n_s);
+      const float expct = (float)m * (float)n_s / (float)nv;
+      const uint32_t r = (uint32_t)ceilf(expct + 3.0f * sqrtf(expct) + 8.0f);
+      if (n_s > 0u && r < n_s) {
+        uint32_t Ts = 0u, need_s = 0u;
+        radix_select<NT>([&](auto f) { f(key[0]); }, r, kmin, kmax, sh, Ts, need_s);
+        const uint32_t T0 = need_s != 0u ? Ts : Ts + 1u;
+        uint32_t cg0 = 0, ce0 = 0;
 #pragma unroll
-          for (int i = 0; i < KPT; ++i) f(key[i]);
-        },
-        m, kmin, kmax, sh, T, need);
+        for (int i = 0; i < KPT; ++i) {
+          cg0 += key[i] > T0;
+          ce0 += key[i] == T0;
+        }
+        // n_cols <= 32768, so both counts fit 16 bits
+        uint32_t tot = 0;
+        const uint32_t ex0 = block_excl_scan_tot<NT>((cg0 << 16) | ce0, sh, tot);
+        const uint32_t G = tot >> 16, E = tot & 0xFFFFu;
+        if (G <= m && m <= G + E) {
+          T = T0;
+          need = m - G;
+          done = true;
+        } else if (G > m && G <= (uint32_t)kCandCap) {
+          uint32_t at = ex0 >> 16;
+#pragma unroll
+          for (int i = 0; i < KPT; ++i) {
+            if (key[i] > T0) {
+              cand_key[at] = key[i];
+              cand_pos[at] = lo + i;
+              ++at;
+            }
+          }
+          __syncthreads();
+          uint32_t Tc = 0u, need_c = 0u;
+          radix_select<NT>(
+              [&](auto f) {
+                for (uint32_t i = tid; i < G; i += NT) f(cand_key[i]);
+              },
+              m, T0 + 1u, kmax, sh, Tc, need_c);
+          // output from the candidates: thread t takes CPT consecutive ones
+          constexpr int CPT = kCandCap / NT;
+          const uint32_t c0 = (uint32_t)tid * CPT;
+          uint32_t ck[CPT];
+          uint32_t cg = 0, ce = 0;
+#pragma unroll
+          for (int i = 0; i < CPT; ++i) {
+            ck[i] = (c0 + i < G) ? cand_key[c0 + i] : 0u;
+            cg += ck[i] > Tc;
+            ce += (need_c != 0u) && (ck[i] == Tc);
+          }
+          const uint32_t excl = block_excl_scan<NT>((cg << 16) | ce, sh);
+          const uint32_t base_e = excl & 0xFFFFu;
+          uint32_t pos = (excl >> 16) + (base_e < need_c ? base_e : need_c);
+          uint32_t er = base_e;
+#pragma unroll
+          for (int i = 0; i < CPT; ++i) {
+            if (ck[i] > Tc) {
+              orow[pos++] = cand_pos[c0 + i] + offset;
+            } else if (need_c != 0u && ck[i] == Tc) {
+              if (er < need_c) orow[pos++] = cand_pos[c0 + i] + offset;
+              ++er;
+            }
+          }
+          for (int32_t i = (int32_t)m + tid; i < k; i += NT) orow[i] = -1;
+          return;
+        }
+      }
+    }
+    if (!done) {
+      radix_select<NT>(
+          [&](auto f) {
+#pragma unroll
+            for (int i = 0; i < KPT; ++i) f(key[i]);
+          },
+          m, kmin, kmax, sh, T, need);
+    }
   }
 
   uint32_t cg = 0, ce = 0;

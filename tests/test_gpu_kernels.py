@@ -241,6 +241,31 @@ def test_topk_big_tie_group_straddles_k(v41):
     assert np.array_equal(got, O.topk(s, k, 128))
 
 
+@pytest.mark.parametrize("L,kpt", [(2048, 8), (4096, 16), (8192, 8), (32768, 32)])
+@pytest.mark.parametrize("layout", ["samples_high", "samples_low", "one_value", "random"])
+def test_topk_sampled_threshold_paths(v41, L, kpt, layout):
+    """Rows whose every kpt-th position (the first position of each thread's
+    range) holds the largest scores, the smallest scores, or where all but a
+    few scores are equal: the sampled threshold then misses the top k (full
+    select), lets too many through (full select) or is the k-th score itself
+    (direct); random rows take the candidate path.  Rows of 32768 sample;
+    the shorter ones check the plain select on the same layouts."""
+    say("topk sampled", L, kpt, layout)
+    rng = np.random.default_rng(L + len(layout))
+    R, k = 3, 512
+    s = rng.uniform(1, 2, (R, L)).astype(np.float32)
+    if layout == "samples_high":
+        s[:, ::kpt] += 10.0
+    elif layout == "samples_low":
+        s[:, ::kpt] -= 10.0
+    elif layout == "one_value":
+        s[:] = 0.5
+        s[:, rng.permutation(L)[:100]] = 3.0
+        s[1, ::7] = -0.0
+    got = run_topk(v41, s, k, 128)
+    assert np.array_equal(got, O.topk(s, k, 128))
+
+
 # ------------------------------------------------------------------ attention
 def run_attn(v41, q, rows_a, rows_b, idx, sink, scale, B, T, use_ws=True):
     """q [B*T, H, D]; rows_a [B, A, D]; rows_b [B, Lb, D] or None; idx [B*T, width]."""
