@@ -141,6 +141,10 @@ def run_indexer(v41, qI, kI, w, start, ratio, cand=None, cand_block=1, B=1, T=No
     (17, 64, 97, 0, 4, 400, 1),         # odd head count, causal prefill
     (1, 32, 50, 10 ** 6, 1, 1, 1),
     (48, 128, 512, 0, 4, 64, 1),
+    (64, 128, 300, 0, 4, 13, 2),        # two sequences of 13 tokens
+    (16, 64, 200, 0, 2, 7, 3),          # three sequences of seven tokens
+    (64, 128, 40, 0, 1, 2, 1),          # two tokens
+    (64, 128, 20, 0, 1, 50, 1),         # the causal bound capped at the row count
 ])
 def test_indexer_parity(v41, HI, DI, L, start, ratio, T, B):
     say("indexer", HI, DI, L, start, ratio, T, B)
