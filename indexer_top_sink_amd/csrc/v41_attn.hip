@@ -787,6 +787,257 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
   }
 }
 
+// ---------------------------------------------------------------- round form
+// The narrow form for D = 512 without the final merge: a workgroup (query,
+// 16 heads, eight wavefronts) takes the query's rows in rounds of 128 (eight
+// 16-row tiles, tile r * 8 + w to wavefront w).  In a round each wavefront
+//  * stores its tile (loaded two rounds ahead into registers, a 1 KB row per
+//    load instruction) into its LDS slot and sends the loads of round + 2;
+//  * computes S^T (16 rows x 16 heads) from the slot and the query tile and
+//    writes it, scaled to the log2 domain, into a shared [head][row] array;
+// then, after a barrier, every wavefront reads the round's 128 scores of the
+// 16 heads, takes the same running maximum and probabilities (identical
+// arithmetic in every wavefront, so they agree exactly), and computes
+// O^T += G^T P^T for its own 64 of the 512 dims over the 128 rows, on
+// v_mfma_f32_16x16x32_bf16 (32 rows per K-step: transposing reads of two
+// tiles), with P as a pair of bf16 terms (high part and remainder).  Each
+// wavefront ends with the finished output of its dims.
+constexpr int kRoundTiles = 8;
+constexpr int kRoundRows = kRoundTiles * kWaveRows;
+constexpr int kSxStride = kRoundRows + 4;  // floats per head row (bank spread)
+
+__global__ __launch_bounds__(kNarrowThreads, 1) void attn_round_kernel(Params p,
+                                                                       int32_t head_groups,
+                                                                       int64_t n_units) {
+  constexpr int D = 512;
+  using WS = WaveSlot<D>;
+  constexpr int kW = kNarrowThreads / kWave;
+  static_assert(kW == kRoundTiles, "one tile per wavefront and round");
+  constexpr int KS = D / 32;                 // QK K-steps (one per tile row register)
+  constexpr int kQStride = 2 * D + 16;
+  constexpr int kDimsPerWave = D / kW;       // 64
+  constexpr int DT = kDimsPerWave / 16;      // 4 output dim-tiles per wavefront
+  static_assert(KS == kWaveRows, "one register per tile row");
+  __shared__ __attribute__((aligned(16))) uint8_t slots[kW * WS::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t qs[kNarrowHeads * kQStride];
+  __shared__ __attribute__((aligned(16))) float sx[kNarrowHeads * kSxStride];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+  const int grp = blockIdx.x >> 3;
+  const int hg = grp % head_groups;
+  const int64_t unit = (int64_t)(grp / head_groups) * 8 + (blockIdx.x & 7);
+  if (unit >= n_units) return;  // whole workgroup
+  const int64_t qi = unit / p.splits;
+  const int split = (int)(unit - qi * p.splits);
+  const int64_t b = qi / p.n_tokens;
+  const int head = hg * kNarrowHeads + r16;
+  const bool head_ok = head < p.n_heads;
+  const int64_t total_rows = p.rows_a_len + p.rows_b_len;
+
+  // tiles are 16 consecutive entries of the idx row (an entry outside the
+  // two sources loads row 0 and is masked); the split's tiles run in rounds
+  const int n_tiles = total_rows > 0 ? (p.width + kWaveRows - 1) / kWaveRows : 0;
+  const int tps = (n_tiles + p.splits - 1) / p.splits;
+  const int t_begin = split * tps;
+  const int t_end = (t_begin + tps < n_tiles) ? t_begin + tps : n_tiles;
+  const int nt = t_end > t_begin ? t_end - t_begin : 0;
+  const int n_rounds = (nt + kRoundTiles - 1) / kRoundTiles;
+  const int32_t* const irow = p.idx + qi * p.idx_ld;
+  const uint16_t* a_base = p.rows_a + b * p.a_bs;
+  const uint16_t* b_base = p.rows_b + b * p.b_bs;
+
+  // this lane's idx entry (row r16) of round r's tile; -1 past the split
+  auto entry = [&](int r) -> int32_t {
+    const int tile = r * kRoundTiles + wave;
+    const int pos = (t_begin + tile) * kWaveRows + r16;
+    return (tile < nt && pos < p.width) ? irow[pos] : -1;
+  };
+  // rb[j] = row j of the tile, lane l holding its chunk l ^ swz(j); returns
+  // the 16-bit validity mask
+  auto load = [&](int32_t raw, u32x4 (&rb)[KS]) -> uint32_t {
+    const bool ok = raw >= 0 && (int64_t)raw < total_rows;
+    const uint32_t vm = (uint32_t)__ballot(ok) & 0xFFFFu;
+    const int32_t my_ix = ok ? raw : 0;
+#pragma unroll
+    for (int j = 0; j < kWaveRows; ++j) {
+      const int64_t ix = __builtin_amdgcn_readlane(my_ix, j);
+      const uint16_t* src =
+          (ix < p.rows_a_len) ? a_base + ix * D : b_base + (ix - p.rows_a_len) * D;
+      rb[j] = *reinterpret_cast<const u32x4*>(src + 8 * (lane ^ WS::swz(j)));
+    }
+    return vm;
+  };
+
+  // ---- prologue: entries of rounds 0 .. 2, the queries, the rows of rounds
+  // 0 and 1 (two rounds of rows stay in flight in registers)
+  const int32_t ent0 = n_rounds > 0 ? entry(0) : -1;
+  const int32_t ent1 = n_rounds > 1 ? entry(1) : -1;
+  int32_t ent_a = n_rounds > 2 ? entry(2) : -1;  // next entries for buffer a
+  int32_t ent_b = -1;                            // ... and for buffer b
+  constexpr int CPR = D / 8;
+  constexpr int kQPer = (kNarrowHeads * CPR + kNarrowThreads - 1) / kNarrowThreads;
+  u32x4 qv[kQPer];
+  const uint16_t* q0 = p.q + (qi * p.n_heads + hg * kNarrowHeads) * D;
+#pragma unroll
+  for (int j = 0; j < kQPer; ++j) {
+    const int e = tid + j * kNarrowThreads;
+    const int h = e / CPR, c = e % CPR;
+    qv[j] = (u32x4){0u, 0u, 0u, 0u};
+    if (e < kNarrowHeads * CPR && hg * kNarrowHeads + h < p.n_heads)
+      qv[j] = *reinterpret_cast<const u32x4*>(q0 + h * D + 8 * c);
+  }
+  u32x4 rb_a[KS], rb_b[KS];
+  uint32_t vm_a = 0u, vm_b = 0u;
+  if (n_rounds > 0) vm_a = load(ent0, rb_a);
+  if (n_rounds > 1) vm_b = load(ent1, rb_b);
+#pragma unroll
+  for (int j = 0; j < kQPer; ++j) {
+    const int e = tid + j * kNarrowThreads;
+    const int h = e / CPR, c = e % CPR;
+    if (e < kNarrowHeads * CPR) *reinterpret_cast<u32x4*>(qs + h * kQStride + 16 * c) = qv[j];
+  }
+
+  const float sink2 = head_ok ? p.sink[head] * kLog2e : 0.0f;
+  const float kNegInf = -__builtin_huge_valf();
+  float m2 = sink2;  // running reference max on the log2 scale (same in every wavefront)
+  float l_part = 0.0f;
+  f32x4 acc[DT];
+#pragma unroll
+  for (int d = 0; d < DT; ++d) acc[d] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  uint8_t* const slot = slots + wave * WS::kBytes;
+  const int st_off = r16 * WS::kStride + 16 * (g ^ WS::swz(r16));  // + 64 kk
+  const uint8_t* const q_frag = qs + r16 * kQStride + 16 * g;      // + 64 kk
+  //  transposing loads: lane (g, j, q) reads 8 bytes of row 4g + j at dims
+  //  4q .. (+ 32 bytes per 16-dim tile) of a slot
+  const int tj = (lane >> 2) & 3, tq = lane & 3;
+  const int tr_row = 4 * g + tj;
+  const uint32_t tr0 = (uint32_t)(size_t)(lds_void*)(size_t)(
+      slots + tr_row * WS::kStride + 16 * ((tq >> 1) ^ WS::swz(tr_row)) + 8 * (tq & 1) +
+      32 * (wave * DT));
+  float* const sx_w = sx + r16 * kSxStride + wave * kWaveRows + 4 * g;  // S^T rows 4g..
+
+  // one round from the rows in rb (validity vm); rb then takes the rows of
+  // round r + 2 (entry ent), and ent the entry of round r + 4
+  auto round = [&](int r, u32x4 (&rb)[KS], uint32_t& vm, int32_t& ent) {
+    // slots and the score array are free once every wavefront finished the
+    // previous round (the first barrier also publishes the query tile)
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < kWaveRows; ++j)
+      *reinterpret_cast<u32x4*>(slot + j * WS::kStride + 16 * lane) = rb[j];
+    const uint32_t vm_cur = vm;
+    if (r + 2 < n_rounds) {
+      vm = load(ent, rb);
+      ent = (r + 4 < n_rounds) ? entry(r + 4) : -1;
+    }
+    // S^T: rows 4g + e of this wavefront's tile, head r16
+    f32x4 sa[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sa[c] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+      const u32x4 qq = *reinterpret_cast<const u32x4*>(q_frag + 64 * kk);
+      const u32x4 av = *reinterpret_cast<const u32x4*>(slot + st_off + 64 * kk);
+      sa[kk & 3] = mfma16x16x32(as_bf16x8(av), as_bf16x8(qq), sa[kk & 3]);
+    }
+    const f32x4 sacc = (sa[0] + sa[1]) + (sa[2] + sa[3]);
+    f32x4 sv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      sv[e] = ((vm_cur >> (4 * g + e)) & 1u) ? sacc[e] * p.scale_log2 : kNegInf;
+    *reinterpret_cast<f32x4*>(sx_w) = sv;
+    lds_barrier();
+
+    // the round's 128 scores of head r16: this lane's K-step values are
+    // rows 32ks + 4g + e (e < 4) and 32ks + 16 + 4g + e, the order of the
+    // transposing reads of tiles 2ks and 2ks + 1
+    f32x4 s_lo[4], s_hi[4];
+    const float* const sx_h = sx + r16 * kSxStride + 4 * g;
+    float mx = kNegInf;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      s_lo[ks] = *reinterpret_cast<const f32x4*>(sx_h + 32 * ks);
+      s_hi[ks] = *reinterpret_cast<const f32x4*>(sx_h + 32 * ks + 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fmaxf(s_lo[ks][e], s_hi[ks][e]));
+    }
+    mx = group_max(mx);
+    if (mx > m2 + kRescaleLog2) {  // the same decision in every lane of a head
+      const float alpha = exp2f(m2 - mx);
+      m2 = mx;
+      l_part *= alpha;
+#pragma unroll
+      for (int d = 0; d < DT; ++d) acc[d] *= alpha;
+    }
+    // probabilities as a bf16 pair (high part and remainder), so P enters
+    // the product with about 16 significant bits
+    bf16x8 pf[4], pr[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = (s_lo[ks][e] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(s_lo[ks][e] - m2);
+        const float p1 = (s_hi[ks][e] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(s_hi[ks][e] - m2);
+        l_part += p0 + p1;
+        const __bf16 h0 = (__bf16)p0, h1 = (__bf16)p1;
+        pf[ks][e] = h0;
+        pf[ks][4 + e] = h1;
+        pr[ks][e] = (__bf16)(p0 - (float)h0);
+        pr[ks][4 + e] = (__bf16)(p1 - (float)h1);
+      }
+    }
+    // O^T[this wavefront's dims][head] += G^T[dims][32 rows] P^T[32 rows][head]
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x2 t[8];
+      tr_load4(t, tr0 + (2 * ks) * WS::kBytes, tr0 + (2 * ks + 1) * WS::kBytes);
+#pragma unroll
+      for (int d = 0; d < DT; ++d) {
+        const u32x4 a = {t[2 * d][0], t[2 * d][1], t[2 * d + 1][0], t[2 * d + 1][1]};
+        acc[d] = mfma16x16x32(as_bf16x8(a), pf[ks], acc[d]);
+        acc[d] = mfma16x16x32(as_bf16x8(a), pr[ks], acc[d]);
+      }
+    }
+  };
+  // entries: buffer a loads rounds 0, 2, 4, ..; buffer b rounds 1, 3, 5, ..
+  if (n_rounds > 3) ent_b = entry(3);
+  for (int r = 0; r < n_rounds; r += 2) {
+    round(r, rb_a, vm_a, ent_a);
+    if (r + 1 < n_rounds) round(r + 1, rb_b, vm_b, ent_b);
+  }
+
+  // ---- epilogue: lane holds O^T[dims 64 wave + 16d + 4g + i][head r16]
+  const float l_tot = group_sum(l_part);
+  if (!head_ok) return;
+  if (p.splits == 1) {
+    const float sink_term = (sink2 == kNegInf) ? 0.0f : exp2f(sink2 - m2);
+    const float den = l_tot + sink_term;
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+    uint16_t* op = p.out + (qi * p.n_heads + head) * D + kDimsPerWave * wave + 4 * g;
+#pragma unroll
+    for (int d = 0; d < DT; ++d) {
+      uint2 v;
+      v.x = f32_to_bf16_bits(acc[d][0] * inv) | (f32_to_bf16_bits(acc[d][1] * inv) << 16);
+      v.y = f32_to_bf16_bits(acc[d][2] * inv) | (f32_to_bf16_bits(acc[d][3] * inv) << 16);
+      *reinterpret_cast<uint2*>(op + 16 * d) = v;
+    }
+  } else {
+    const int64_t slot_i = (qi * p.splits + split) * p.n_heads + head;
+    float* po = p.part_o + slot_i * D + kDimsPerWave * wave + 4 * g;
+#pragma unroll
+    for (int d = 0; d < DT; ++d) *reinterpret_cast<f32x4*>(po + 16 * d) = acc[d];
+    if (wave == 0 && g == 0) {
+      p.part_ml[2 * slot_i] = m2;
+      p.part_ml[2 * slot_i + 1] = l_tot;
+    }
+  }
+}
+
 // Merge the row splits of each (query, head): M = max_s m_s,
 // den = sum_s l_s 2^(m_s - M) + 2^(sink - M), o = sum_s O_s 2^(m_s - M) / den.
 template <int D>
@@ -860,8 +1111,17 @@ hipError_t launch_d(const AttnArgs& a, int splits, hipStream_t s) {
     const int64_t units = nq * splits;
     const int64_t blocks = 8 * hg * ((units + 7) / 8);
     if (blocks > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attn_narrow_kernel<D>), dim3((unsigned)blocks), dim3(kNarrowThreads), 0,
-                       s, p, hg, units);
+    // a workgroup whose rows fit one round (at most 8 tiles) takes the round
+    // form: no final merge; with more rounds its two barriers per round cost
+    // more than the merge saves (measured), so the wavefronts work alone
+    const int64_t tiles = (a.width + kWaveRows - 1) / kWaveRows;
+    const bool one_round = (tiles + splits - 1) / splits <= kRoundTiles;
+    if (D == 512 && one_round)
+      hipLaunchKernelGGL(attn_round_kernel, dim3((unsigned)blocks), dim3(kNarrowThreads), 0, s,
+                         p, hg, units);
+    else
+      hipLaunchKernelGGL((attn_narrow_kernel<D>), dim3((unsigned)blocks), dim3(kNarrowThreads),
+                         0, s, p, hg, units);
   } else {
     // two workgroups per CU with a two-tile ring each (a four-tile ring with
     // one workgroup per CU measured slower on row-split decode shapes)

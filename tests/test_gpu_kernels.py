@@ -305,6 +305,8 @@ def oracle_attn(q, rows_a, rows_b, idx, sink, scale, B, T):
     (1, 12, 4, 64, 12, 4, 10, True),           # the tiny layer
     (2, 3, 70, 128, 50, 60, 97, True),         # heads over two groups, ragged
     (1, 5, 16, 256, 33, 0, 33, True),          # no compressed rows
+    (1, 2, 64, 512, 64, 200, 120, True),       # one round of 8 tiles per workgroup
+    (2, 1, 40, 512, 128, 300, 640, True),      # one round per split, a partial head group
 ])
 def test_attn_parity(v41, B, T, H, D, A, Lb, width, use_ws):
     say("attn", B, T, H, D, A, Lb, width, use_ws)
@@ -336,9 +338,11 @@ def test_attn_all_absent_and_one_row(v41):
     assert_attn_close(got, want, "one row")
 
 
-def test_attn_large_logits(v41):
-    """Scores far from zero exercise the running max (no overflow)."""
-    H, D, A = 64, 512, 300
+@pytest.mark.parametrize("A", [300, 120])
+def test_attn_large_logits(v41, A):
+    """Scores far from zero exercise the running max (no overflow); 300 rows
+    take two rounds per split (wavefronts merged at the end), 120 one round."""
+    H, D = 64, 512
     rng = np.random.default_rng(4)
     q = bf16_of(rng.standard_normal((1, H, D)) * 4)
     rows_a = bf16_of(rng.standard_normal((1, A, D)) * 4)
