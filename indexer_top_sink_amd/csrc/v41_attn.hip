@@ -263,8 +263,11 @@ __global__ __launch_bounds__(kThreads, NS == 2 ? 2 : 1) void attn_kernel(Params 
   const int wave = tid >> 6;
   const int r16 = lane & 15;
   const int g = lane >> 4;
-  const int64_t qi = blockIdx.x / p.splits;
-  const int split = (int)(blockIdx.x - qi * p.splits);
+  // queries in reverse order: in a chunk the later tokens see more rows, so
+  // the longest workgroups start first and the short ones fill the tail
+  const int64_t unit = (int64_t)(gridDim.x - 1 - blockIdx.x);
+  const int64_t qi = unit / p.splits;
+  const int split = (int)(unit - qi * p.splits);
   const int64_t b = qi / p.n_tokens;
   const int head = blockIdx.y * kHeadsPerBlock + 16 * wave + r16;
   const bool head_ok = head < p.n_heads;
