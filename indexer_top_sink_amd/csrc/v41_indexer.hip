@@ -135,9 +135,12 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15;
   const int g = lane >> 4;
-  const int64_t q = blockIdx.x / blocks_per_query;
+  // queries in reverse order: in a chunk the later tokens see more keys, so
+  // the longest workgroups start first and the short ones fill the tail
+  const int32_t unit = score_blocks - 1 - (int32_t)blockIdx.x;
+  const int64_t q = unit / blocks_per_query;
   const int wpq = blocks_per_query * kWaves;
-  const int part = (int)(blockIdx.x - q * blocks_per_query) * kWaves + wave;
+  const int part = (int)(unit - q * blocks_per_query) * kWaves + wave;
   const int64_t b = q / n_tokens;
   const int64_t t = q - b * n_tokens;
   // position of the token: the call's start_pos, or read on the device
