@@ -135,9 +135,19 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r16 = lane & 15;
   const int g = lane >> 4;
-  // queries in reverse order: in a chunk the later tokens see more keys, so
-  // the longest workgroups start first and the short ones fill the tail
-  const int32_t unit = score_blocks - 1 - (int32_t)blockIdx.x;
+  // Decode (one token per sequence, a multiple of 8 queries): the
+  // workgroups of query q sit on XCD q mod 8 (dispatch is round-robin over
+  // the 8 XCDs), where the top-k and the attention of that query run, so
+  // they read its scores from that XCD's L2.  Otherwise queries go in
+  // reverse order: in a chunk the later tokens see more keys, so the longest
+  // workgroups start first and the short ones fill the tail.
+  int32_t unit;
+  if (n_tokens == 1 && (score_blocks / blocks_per_query) % 8 == 0) {
+    const int32_t xcd = (int32_t)blockIdx.x & 7, j = (int32_t)blockIdx.x >> 3;
+    unit = (8 * (j / blocks_per_query) + xcd) * blocks_per_query + j % blocks_per_query;
+  } else {
+    unit = score_blocks - 1 - (int32_t)blockIdx.x;
+  }
   const int64_t q = unit / blocks_per_query;
   const int wpq = blocks_per_query * kWaves;
   const int part = (int)(unit - q * blocks_per_query) * kWaves + wave;
