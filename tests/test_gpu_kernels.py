@@ -137,6 +137,7 @@ def run_indexer(v41, qI, kI, w, start, ratio, cand=None, cand_block=1, B=1, T=No
 @pytest.mark.parametrize("HI,DI,L,start,ratio,T,B", [
     (64, 128, 1000, 4095, 4, 1, 1),     # decode, ragged tail
     (64, 128, 333, 10 ** 6, 1, 1, 3),   # batch of decodes
+    (64, 128, 1000, 4095, 4, 1, 8),     # eight decodes: each query's workgroups on one XCD
     (2, 32, 4, 0, 4, 12, 1),            # the tiny layer's prefill
     (17, 64, 97, 0, 4, 400, 1),         # odd head count, causal prefill
     (1, 32, 50, 10 ** 6, 1, 1, 1),
