@@ -52,8 +52,10 @@ struct TopkShared {
 // Capacity of the sampled select's candidate buffer (keys and positions).
 constexpr int kCandCap = 4096;
 
-// Exclusive scan of one value per thread over the block (two barriers).
-template <int NT>
+// Exclusive scan of one value per thread over the block (two barriers; the
+// last scan of a kernel skips the second, which only protects sh.red for a
+// later use).
+template <int NT, bool kLast = false>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, TopkShared<NT>& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t incl = wave_incl_scan_u32(v);
@@ -61,7 +63,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, TopkShared<NT>& 
   __syncthreads();
   uint32_t base = 0;
   for (int w = 0; w < wave; ++w) base += sh.red[0][w];
-  __syncthreads();
+  if constexpr (!kLast) __syncthreads();
   return base + incl - v;
 }
 
@@ -84,8 +86,9 @@ __device__ __forceinline__ uint32_t block_excl_scan_tot(uint32_t v, TopkShared<N
   return base + incl - v;
 }
 
-// Count, min and max of the valid keys over the block (two barriers).
-template <int NT>
+// Count, min and max of the valid keys over the block (two barriers; with
+// kTrail false the caller orders any later write of sh.red itself).
+template <int NT, bool kTrail = true>
 __device__ __forceinline__ void block_stats(uint32_t nv, uint32_t kmin, uint32_t kmax,
                                             TopkShared<NT>& sh, uint32_t& o_nv,
                                             uint32_t& o_min, uint32_t& o_max) {
@@ -107,19 +110,22 @@ __device__ __forceinline__ void block_stats(uint32_t nv, uint32_t kmin, uint32_t
     o_min = min(o_min, sh.red[1][w]);
     o_max = max(o_max, sh.red[2][w]);
   }
-  __syncthreads();
+  if constexpr (kTrail) __syncthreads();
 }
 
 // Radix select over d = key - kmin of the valid keys: returns T (a key) and
 // `need`, the number of keys equal to T that belong to the top m.
 // for_keys(f) calls f(key) for every key the thread owns.
-template <int NT, class ForKeys>
+template <int NT, class ForKeys, bool kPreCleared = false>
 __device__ __forceinline__ void radix_select(ForKeys for_keys, uint32_t m, uint32_t kmin,
                                              uint32_t kmax, TopkShared<NT>& sh, uint32_t& T,
                                              uint32_t& need) {
   const int tid = threadIdx.x, lane = tid & 63;
   const uint32_t range = kmax - kmin;
   if (range == 0u) {
+    // without the clearing barrier this is the caller's only barrier between
+    // its statistics and its next use of sh.red
+    if constexpr (kPreCleared) __syncthreads();
     T = kmax;
     need = m;
     return;
@@ -127,8 +133,10 @@ __device__ __forceinline__ void radix_select(ForKeys for_keys, uint32_t m, uint3
   const int top = 31 - __clz(range);
   int shift = top > 7 ? top - 7 : 0;
   uint32_t prefix = 0u, pmask = 0u, need_r = m;
-  for (int i = tid; i < kHistCopies * kHistStride; i += NT) sh.hist[0][i] = 0u;
-  __syncthreads();
+  if constexpr (!kPreCleared) {
+    for (int i = tid; i < kHistCopies * kHistStride; i += NT) sh.hist[0][i] = 0u;
+    __syncthreads();
+  }
   for (int pass = 0;; ++pass) {
     uint32_t* const hist = sh.hist[pass & 1];
     // the other copy was last read before the previous pass's final barrier
@@ -235,8 +243,16 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(const float* __restrict__ 
     }
   }
   uint32_t nv, kmin, kmax;
-  block_stats<NT>(nv_t, kmin_t, kmax_t, sh, nv, kmin, kmax);
+  // the first radix histogram is cleared before the statistics' barrier,
+  // which then also publishes it; without the sampled threshold the select
+  // (or, when every valid key is taken, one barrier) follows the statistics
+  // before anything rewrites sh.red
+  for (int i = tid; i < kHistCopies * kHistStride; i += NT) sh.hist[0][i] = 0u;
+  block_stats<NT, (KPT >= 32)>(nv_t, kmin_t, kmax_t, sh, nv, kmin, kmax);
   const uint32_t m = nv < (uint32_t)k ? nv : (uint32_t)k;
+  if constexpr (KPT < 32) {
+    if (nv <= (uint32_t)k) __syncthreads();
+  }
 
   uint32_t T = 0u, need = 0u;
   if (nv > (uint32_t)k) {
@@ -302,7 +318,7 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(const float* __restrict__ 
             cg += ck[i] > Tc;
             ce += (need_c != 0u) && (ck[i] == Tc);
           }
-          const uint32_t excl = block_excl_scan<NT>((cg << 16) | ce, sh);
+          const uint32_t excl = block_excl_scan<NT, true>((cg << 16) | ce, sh);
           const uint32_t base_e = excl & 0xFFFFu;
           uint32_t pos = (excl >> 16) + (base_e < need_c ? base_e : need_c);
           uint32_t er = base_e;
@@ -321,12 +337,14 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(const float* __restrict__ 
       }
     }
     if (!done) {
-      radix_select<NT>(
-          [&](auto f) {
+      auto all_keys = [&](auto f) {
 #pragma unroll
-            for (int i = 0; i < KPT; ++i) f(key[i]);
-          },
-          m, kmin, kmax, sh, T, need);
+        for (int i = 0; i < KPT; ++i) f(key[i]);
+      };
+      if constexpr (KPT >= 32)
+        radix_select<NT>(all_keys, m, kmin, kmax, sh, T, need);
+      else
+        radix_select<NT, decltype(all_keys), true>(all_keys, m, kmin, kmax, sh, T, need);
     }
   }
 
@@ -337,7 +355,7 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(const float* __restrict__ 
     ce += (need != 0u) && (key[i] == T);
   }
   // n_cols <= 32768, so both counts fit 16 bits
-  const uint32_t excl = block_excl_scan<NT>((cg << 16) | ce, sh);
+  const uint32_t excl = block_excl_scan<NT, true>((cg << 16) | ce, sh);
   const uint32_t base_e = excl & 0xFFFFu;
   uint32_t pos = (excl >> 16) + (base_e < need ? base_e : need);
   uint32_t er = base_e;
