@@ -207,7 +207,8 @@ def tie_scores(rng, R, L):
                                           (4, 1000, 512, 128), (2, 4096, 512, 128),
                                           (2, 5000, 100, 0), (2, 32768, 512, 128),
                                           (1, 40000, 2048, 7), (64, 8192, 512, 128),
-                                          (8, 300, 2048, 3)])
+                                          (8, 300, 2048, 3), (6, 512, 64, 128),
+                                          (3, 500, 100, 7), (4, 64, 16, 0)])
 def test_topk_parity_ties(v41, R, L, k, offset):
     say("topk", R, L, k, offset)
     rng = np.random.default_rng(R * 7 + L)
@@ -234,6 +235,16 @@ def test_topk_all_excluded_and_signed_zeros(v41):
     assert np.array_equal(got, want)
     assert np.all(got[0] == -1) and np.all(got[1] == -1)
     assert got[2].tolist() == [5 + j for j in range(512)]
+
+
+@pytest.mark.parametrize("L", [512, 1024])
+def test_topk_all_equal_scores(v41, L):
+    """Every score equal (one radix bin from the start): the lowest k
+    positions, with short rows on the one-wavefront select."""
+    s = np.full((3, L), 0.75, dtype=np.float32)
+    s[1, ::3] = -np.inf
+    got = run_topk(v41, s, 100, 128)
+    assert np.array_equal(got, O.topk(s, 100, 128))
 
 
 def test_topk_big_tie_group_straddles_k(v41):
