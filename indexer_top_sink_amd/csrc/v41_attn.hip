@@ -403,6 +403,39 @@ __global__ __launch_bounds__(kThreads, NS == 2 ? 2 : 1) void attn_kernel(Params 
   // ---- epilogue: lane holds O^T[dims 16mt + 4g + i][head r16]
   float l_tot = l_part;
   l_tot = group_sum(l_tot);
+  if constexpr (D == 512) {
+    if (p.splits == 1) {
+      // the 64 heads' bf16 rows go through the (now idle) tile buffers and
+      // leave as the query's contiguous output block, 16 bytes per lane
+      // (8-byte stores spread over 16 head rows measured slow); rows are
+      // padded by 16 bytes so the 16 head rows of a store hit distinct banks
+      constexpr int kOStride = 2 * D + 16;
+      static_assert(kHeadsPerBlock * kOStride <= NS * TL::kBufBytes, "output staging");
+      const float sink_term = (sink2 == kNegInf) ? 0.0f : exp2f(sink2 - m2);
+      const float den = l_tot + sink_term;
+      const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+      lds_barrier();  // every wavefront is done with the last tile
+      uint8_t* const orow = tiles + (16 * wave + r16) * kOStride + 8 * g;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        uint2 v;
+        v.x = f32_to_bf16_bits(acc_o[mt][0] * inv) | (f32_to_bf16_bits(acc_o[mt][1] * inv) << 16);
+        v.y = f32_to_bf16_bits(acc_o[mt][2] * inv) | (f32_to_bf16_bits(acc_o[mt][3] * inv) << 16);
+        *reinterpret_cast<uint2*>(orow + 32 * mt) = v;
+      }
+      lds_barrier();
+      const int hbase = blockIdx.y * kHeadsPerBlock;
+      const int nh = (p.n_heads - hbase < kHeadsPerBlock) ? p.n_heads - hbase : kHeadsPerBlock;
+      uint16_t* const qout = p.out + (qi * p.n_heads + hbase) * D;
+      constexpr int kCPR = D / 8;  // 16-byte chunks per head row
+      for (int e = tid; e < nh * kCPR; e += kThreads) {
+        const int h = e / kCPR, c = e - h * kCPR;
+        *reinterpret_cast<u32x4*>(qout + h * D + 8 * c) =
+            *reinterpret_cast<const u32x4*>(tiles + h * kOStride + 16 * c);
+      }
+      return;
+    }
+  }
   if (!head_ok) return;
   if (p.splits == 1) {
     const float sink_term = (sink2 == kNegInf) ? 0.0f : exp2f(sink2 - m2);
