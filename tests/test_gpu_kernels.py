@@ -319,6 +319,7 @@ def oracle_attn(q, rows_a, rows_b, idx, sink, scale, B, T):
     (1, 5, 16, 256, 33, 0, 33, True),          # no compressed rows
     (1, 2, 64, 512, 64, 200, 120, True),       # one round of 8 tiles per workgroup
     (2, 1, 40, 512, 128, 300, 640, True),      # one round per split, a partial head group
+    (1, 200, 70, 512, 64, 100, 64, True),      # wide form at 512 dims, a 6-head second group
 ])
 def test_attn_parity(v41, B, T, H, D, A, Lb, width, use_ws):
     say("attn", B, T, H, D, A, Lb, width, use_ws)
