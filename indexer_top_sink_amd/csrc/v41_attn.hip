@@ -142,10 +142,17 @@ __device__ __forceinline__ void lds_barrier() {
 // order) into list and returns how many there are.  Every thread of the
 // workgroup (kW wavefronts) calls it; each wavefront scans a contiguous share
 // of the row.
-template <int kW>
+struct NoHook {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+// mid() runs between the two barriers (every wavefront has passed the first,
+// none the second).
+template <int kW, class Mid = NoHook>
 __device__ __forceinline__ uint32_t compact_idx(const int32_t* __restrict__ irow, int width,
                                                 int64_t total_rows, int32_t* list,
-                                                uint32_t* wave_cnt, int wave, int lane) {
+                                                uint32_t* wave_cnt, int wave, int lane,
+                                                Mid mid = Mid()) {
   const int per_wave = ((width + kW * kWave - 1) / (kW * kWave)) * kWave;
   const int w0 = wave * per_wave;
   int w1 = w0 + per_wave;
@@ -159,6 +166,7 @@ __device__ __forceinline__ uint32_t compact_idx(const int32_t* __restrict__ irow
   }
   if (lane == 0) wave_cnt[wave] = cnt;
   __syncthreads();
+  mid();
   uint32_t base = 0;
   for (int w = 0; w < wave; ++w) base += wave_cnt[w];
   for (int i0 = w0; i0 < w1; i0 += kWave) {
@@ -274,9 +282,33 @@ __global__ __launch_bounds__(kThreads, NS == 2 ? 2 : 1) void attn_kernel(Params 
   const int64_t total_rows = p.rows_a_len + p.rows_b_len;
 
   // ---- query fragments (B operand of S^T = G Q^T): head r16, dims 32kk+8g..
-  // requested before the idx row, so the two latencies overlap
+  // requested before the idx row, so the two latencies overlap.  For D = 512
+  // each wavefront pulls its 16 head rows (16 KB, contiguous) into its part
+  // of the idle tile buffers with 1 KB direct-to-LDS loads and reads the
+  // fragments back between the compaction's barriers (whose second barrier
+  // then frees the buffers for the gather); 16-byte register loads spread
+  // over 16 head rows measured slow.
+  constexpr int kQStride = 2 * D + 16;  // padded rows: the fragment reads spread over banks
   bf16x8 qf[KS];
-  {
+  uint32_t n_valid;
+  if constexpr (D == 512) {
+    static_assert(kHeadsPerBlock * kQStride <= NS * TL::kBufBytes, "query staging");
+    const int hbase = blockIdx.y * kHeadsPerBlock;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int h = 16 * wave + j;
+      const int hh = (hbase + h < p.n_heads) ? hbase + h : 0;  // finite rows past n_heads
+      dma16(p.q + (qi * p.n_heads + hh) * D + 8 * lane, tiles + h * kQStride);
+    }
+    n_valid = compact_idx<kThreads / kWave>(
+        p.idx + qi * p.idx_ld, p.width, total_rows, list, wave_cnt, wave, lane, [&]() {
+          wait_vm<0>();
+          const uint8_t* const qrow = tiles + (16 * wave + r16) * kQStride + 16 * g;
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk)
+            qf[kk] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + 64 * kk));
+        });
+  } else {
     const uint16_t* qp = p.q + (qi * p.n_heads + (head_ok ? head : 0)) * D + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) {
@@ -284,9 +316,9 @@ __global__ __launch_bounds__(kThreads, NS == 2 ? 2 : 1) void attn_kernel(Params 
       if (head_ok) v = *reinterpret_cast<const u32x4*>(qp + 32 * kk);
       qf[kk] = as_bf16x8(v);
     }
+    n_valid = compact_idx<kThreads / kWave>(p.idx + qi * p.idx_ld, p.width, total_rows, list,
+                                            wave_cnt, wave, lane);
   }
-  const uint32_t n_valid = compact_idx<kThreads / kWave>(p.idx + qi * p.idx_ld, p.width,
-                                                         total_rows, list, wave_cnt, wave, lane);
   const int n_tiles = (int)((n_valid + kTile - 1) / kTile);
   const int tps = (n_tiles + p.splits - 1) / p.splits;
   const int t_begin = split * tps;
