@@ -21,8 +21,9 @@
 // The epilogue applies ReLU and the weights in f32, sums the 4 heads a lane
 // holds per tile, then across the 4 lane groups with two xor-shuffles.  Keys
 // past the causal bound are never loaded and score -inf; with a candidate mask
-// a last pass overwrites the masked positions with -inf (their products were
-// computed and are discarded).
+// each block's mask byte is requested just before the next stage's loads (so
+// its wait leaves them in flight) and the epilogue writes -inf for a masked
+// position (its products were computed and are discarded).
 #include "v41_common.h"
 #include "v41_front.h"
 
@@ -224,6 +225,12 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(
         else wait_vmcnt<0>();
         u32x4 kf[KS];
         lds_read_ks<KS>(kf, off, ring_lds + s * KT::kBytes);
+        // the block's mask byte, requested before the next stage's loads so
+        // that waiting for it leaves those in flight
+        const int jm = (part + i * wpq) * 16 + r16;
+        uint32_t keep = 1u;
+        if (cand != nullptr && g == 0 && jm < live_end)
+          keep = cand[q * cand_width + (uint32_t)jm / (uint32_t)cand_block];
         if (i + kStages < nw)
           issue_block<DI, kAux>(kb, (part + (i + kStages) * wpq) * 16, live_end, lane,
                                 ring + s * KT::kBytes);
@@ -252,19 +259,11 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(
           sum = __uint_as_float(t[0]) + __uint_as_float(t[1]);
         }
         const int j = (part + i * wpq) * 16 + r16;
-        if (g == 0 && j < n_rows) srow[j] = j < live_end ? sum : kNegInf;
+        if (g == 0 && j < n_rows) srow[j] = (j < live_end && keep != 0u) ? sum : kNegInf;
       }
     }
   }
 
-  // ---- candidate mask: the same lanes overwrite their masked scores
-  if (cand != nullptr && g == 0) {
-    const uint8_t* __restrict__ crow = cand + q * cand_width;
-    for (int i = 0; i < nw; ++i) {
-      const int j = (part + i * wpq) * 16 + r16;
-      if (j < live_end && crow[(uint32_t)j / (uint32_t)cand_block] == 0) srow[j] = kNegInf;
-    }
-  }
 }
 
 template <int DI, int NT>
