@@ -322,11 +322,12 @@ hipError_t launch_indexer_scores_front(const uint16_t* qI, const uint16_t* kI, i
     // nothing to score: the front work alone
     return launch_decode_front(*front_args, s);
   }
-  // Workgroups per query: about 384 over the whole grid (1.5 per CU; up to 3
-  // fit in LDS), the best measured for decode at 16 and 64 sequences, but at
+  // Workgroups per query: about 512 over the whole grid (2 per CU; up to 3
+  // fit in LDS), the best measured for decode at 16 and 64 sequences (with
+  // the XCD placement: 256 clearly slower, 384 and 768 slightly), but at
   // least two 16-key blocks for each wavefront.
   const int64_t nbt = (n_rows + 15) / 16;
-  int64_t bpq = (384 + nq / 2) / nq;
+  int64_t bpq = (512 + nq / 2) / nq;
   const int64_t bpq_max = nbt / (2 * kWaves);
   if (bpq > bpq_max) bpq = bpq_max;
   if (bpq < 1) bpq = 1;
