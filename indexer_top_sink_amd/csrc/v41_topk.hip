@@ -11,8 +11,9 @@
 //     barrier);
 //  2. radix select of the k-th largest key T: digits of 8 bits of
 //     (key - min), starting at the top bit of (max - min), so the first pass
-//     already spreads over the bins; the LDS histogram is replicated 8 ways
-//     across lanes so that equal digits do not serialise on one word; two
+//     already spreads over the bins; the LDS histogram is replicated across
+//     lanes (2 to 8 copies by keys per thread) so that equal digits do not
+//     serialise on one word; two
 //     histograms alternate so clearing the next one overlaps the counting,
 //     and the first wavefront sums the copies while it scans (two barriers
 //     per pass).  The passes stop as soon as the bin holding the k-th key is
@@ -40,11 +41,12 @@ __device__ __forceinline__ uint32_t score_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int NT>
+template <int NT, int HC = kHistCopies>
 struct TopkShared {
+  static constexpr int kCopies = HC;
   // alternate passes (the idle one is cleared); copy c of bin b at
   // c * kHistStride + b, so the copies of one bin sit in distinct banks
-  uint32_t hist[2][kHistCopies * kHistStride];
+  uint32_t hist[2][HC * kHistStride];
   uint32_t red[3][NT / kWave];
   uint32_t digit, above, bin;
 };
@@ -55,8 +57,8 @@ constexpr int kCandCap = 4096;
 // Exclusive scan of one value per thread over the block (two barriers; the
 // last scan of a kernel skips the second, which only protects sh.red for a
 // later use).
-template <int NT, bool kLast = false>
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, TopkShared<NT>& sh) {
+template <int NT, bool kLast = false, int HC>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, TopkShared<NT, HC>& sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t incl = wave_incl_scan_u32(v);
   if (lane == kWave - 1) sh.red[0][wave] = incl;
@@ -68,8 +70,8 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, TopkShared<NT>& 
 }
 
 // The same, also returning the block total.
-template <int NT>
-__device__ __forceinline__ uint32_t block_excl_scan_tot(uint32_t v, TopkShared<NT>& sh,
+template <int NT, int HC>
+__device__ __forceinline__ uint32_t block_excl_scan_tot(uint32_t v, TopkShared<NT, HC>& sh,
                                                         uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const uint32_t incl = wave_incl_scan_u32(v);
@@ -88,9 +90,9 @@ __device__ __forceinline__ uint32_t block_excl_scan_tot(uint32_t v, TopkShared<N
 
 // Count, min and max of the valid keys over the block (two barriers; with
 // kTrail false the caller orders any later write of sh.red itself).
-template <int NT, bool kTrail = true>
+template <int NT, bool kTrail = true, int HC>
 __device__ __forceinline__ void block_stats(uint32_t nv, uint32_t kmin, uint32_t kmax,
-                                            TopkShared<NT>& sh, uint32_t& o_nv,
+                                            TopkShared<NT, HC>& sh, uint32_t& o_nv,
                                             uint32_t& o_min, uint32_t& o_max) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   nv = wave_sum_u32(nv);
@@ -116,9 +118,9 @@ __device__ __forceinline__ void block_stats(uint32_t nv, uint32_t kmin, uint32_t
 // Radix select over d = key - kmin of the valid keys: returns T (a key) and
 // `need`, the number of keys equal to T that belong to the top m.
 // for_keys(f) calls f(key) for every key the thread owns.
-template <int NT, class ForKeys, bool kPreCleared = false>
+template <int NT, class ForKeys, bool kPreCleared = false, int HC>
 __device__ __forceinline__ void radix_select(ForKeys for_keys, uint32_t m, uint32_t kmin,
-                                             uint32_t kmax, TopkShared<NT>& sh, uint32_t& T,
+                                             uint32_t kmax, TopkShared<NT, HC>& sh, uint32_t& T,
                                              uint32_t& need) {
   const int tid = threadIdx.x, lane = tid & 63;
   const uint32_t range = kmax - kmin;
@@ -134,14 +136,14 @@ __device__ __forceinline__ void radix_select(ForKeys for_keys, uint32_t m, uint3
   int shift = top > 7 ? top - 7 : 0;
   uint32_t prefix = 0u, pmask = 0u, need_r = m;
   if constexpr (!kPreCleared) {
-    for (int i = tid; i < kHistCopies * kHistStride; i += NT) sh.hist[0][i] = 0u;
+    for (int i = tid; i < HC * kHistStride; i += NT) sh.hist[0][i] = 0u;
     __syncthreads();
   }
   for (int pass = 0;; ++pass) {
     uint32_t* const hist = sh.hist[pass & 1];
     // the other copy was last read before the previous pass's final barrier
-    for (int i = tid; i < kHistCopies * kHistStride; i += NT) sh.hist[(pass + 1) & 1][i] = 0u;
-    uint32_t* const myhist = hist + (lane % kHistCopies) * kHistStride;
+    for (int i = tid; i < HC * kHistStride; i += NT) sh.hist[(pass + 1) & 1][i] = 0u;
+    uint32_t* const myhist = hist + (lane % HC) * kHistStride;
     // a run of equal digits among the thread's keys (its positions are
     // contiguous, so tied scores form runs) costs one atomic
     uint32_t run_bin = 0u, run_cnt = 0u;
@@ -168,7 +170,7 @@ __device__ __forceinline__ void radix_select(ForKeys for_keys, uint32_t m, uint3
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int cp = 0; cp < kHistCopies; ++cp) c[j] += hist[cp * kHistStride + 255 - 4 * lane - j];
+        for (int cp = 0; cp < HC; ++cp) c[j] += hist[cp * kHistStride + 255 - 4 * lane - j];
       const uint32_t s = c[0] + c[1] + c[2] + c[3];
       const uint32_t incl = wave_incl_scan_u32(s);
       const uint32_t excl = incl - s;
@@ -207,7 +209,10 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(const float* __restrict__ 
                                                       int32_t k, int32_t offset,
                                                       int32_t* __restrict__ idx,
                                                       int64_t idx_ld) {
-  __shared__ TopkShared<NT> sh;
+  // histogram copies: fewer copies make the bin scan cheaper, more spread
+  // the atomics of many keys per thread (measured: 2 best at 8 keys per
+  // thread, 4 at 32)
+  __shared__ TopkShared<NT, (KPT <= 8 ? 2 : 4)> sh;
   constexpr int kCandN = KPT >= 32 ? kCandCap : 1;  // only long rows sample
   __shared__ uint32_t cand_key[kCandN];
   __shared__ int32_t cand_pos[kCandN];
@@ -247,7 +252,7 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(const float* __restrict__ 
   // which then also publishes it; without the sampled threshold the select
   // (or, when every valid key is taken, one barrier) follows the statistics
   // before anything rewrites sh.red
-  for (int i = tid; i < kHistCopies * kHistStride; i += NT) sh.hist[0][i] = 0u;
+  for (int i = tid; i < sh.kCopies * kHistStride; i += NT) sh.hist[0][i] = 0u;
   block_stats<NT, (KPT >= 32)>(nv_t, kmin_t, kmax_t, sh, nv, kmin, kmax);
   const uint32_t m = nv < (uint32_t)k ? nv : (uint32_t)k;
   if constexpr (KPT < 32) {
