@@ -503,8 +503,8 @@ __global__ __launch_bounds__(kThreads, NS == 2 ? 2 : 1) void attn_kernel(Params 
 // without partial results.  The workgroups of one row set sit 8 apart in the
 // grid (one XCD under round-robin dispatch) and share its rows in that L2.
 // Eight wavefronts (two per SIMD, so one hides the other's latencies) each
-// work alone on 16-row tiles handed out by an LDS counter, with their own
-// online softmax, and are merged at the end:
+// work alone on every eighth 16-row tile, with their own online softmax, and
+// are merged at the end:
 //  * the 16 heads' queries sit in LDS and feed the QK B operand;
 //  * a tile's rows are loaded one tile ahead into registers.  For D = 512 a
 //    load instruction fetches one whole 1 KB row (a lane per 16-byte chunk):
@@ -592,7 +592,6 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
   __shared__ int32_t ixs[kMaxWidth];  // the idx row, entries outside the sources as -1
   __shared__ float xm[kW][kNarrowHeads];
   __shared__ float xl[kW][kNarrowHeads];
-  __shared__ uint32_t tile_ctr;  // tiles handed out after each wavefront's first
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -618,14 +617,8 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
   const int t_end = (t_begin + tps < n_tiles) ? t_begin + tps : n_tiles;
   const int nt = t_end > t_begin ? t_end - t_begin : 0;
   const int32_t* const irow = p.idx + qi * p.idx_ld;
-  // the next tile goes to whichever wavefront asks first (the second
-  // wavefront of a SIMD gets fewer issue slots, so a fixed deal leaves it
-  // behind); each wavefront's first tile is its own index
-  auto grab = [&]() -> int {
-    uint32_t t = 0u;
-    if (lane == 0) t = atomicAdd(&tile_ctr, 1u);
-    return kW + (int)__builtin_amdgcn_readfirstlane(t);
-  };
+  // wavefront w takes tiles w, w + 8, ... (handing tiles out through an LDS
+  // counter measured 2% slower with this prologue)
 
   // ---- a lane's share of a tile: entry r16 of the tile.  Returns the tile's
   // 16-bit validity mask (bit r: entry r names a row).
@@ -661,8 +654,6 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
   // ---- prologue: the first tile's entries, the idx row and the 16 heads'
   // queries (zero rows past n_heads) are all requested before anything waits,
   // then the first tile's rows go out; one barrier publishes the LDS copies
-  // and the tile counter
-  if (tid == 0) tile_ctr = 0u;
   int cur = wave;
   int32_t raw0 = -1;
   if (cur < nt && entry(cur) < p.width) raw0 = irow[entry(cur)];
@@ -719,7 +710,7 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
       slot + tr_row * WS::kStride + 16 * ((tq >> 1) ^ WS::swz(tr_row)) + 8 * (tq & 1));
 
   while (cur < nt) {
-    const int nxt = grab();
+    const int nxt = cur + kW;
     uint32_t vm_nxt = 0u;
     // S^T: rows 4g + e of the tile, head r16
     f32x4 sa[4];
