@@ -320,6 +320,9 @@ def oracle_attn(q, rows_a, rows_b, idx, sink, scale, B, T):
     (1, 2, 64, 512, 64, 200, 120, True),       # one round of 8 tiles per workgroup
     (2, 1, 40, 512, 128, 300, 640, True),      # one round per split, a partial head group
     (1, 200, 70, 512, 64, 100, 64, True),      # wide form at 512 dims, a 6-head second group
+    (1, 1, 64, 512, 128, 4000, 2048, True),    # widest row: 16 splits of one round each
+    (2, 1, 64, 512, 128, 3000, 2048, False),   # widest row unsplit: 16 tiles per wavefront
+    (1, 256, 64, 64, 256, 3000, 2048, True),   # widest row in the wide form (compacted list)
 ])
 def test_attn_parity(v41, B, T, H, D, A, Lb, width, use_ws):
     say("attn", B, T, H, D, A, Lb, width, use_ws)
