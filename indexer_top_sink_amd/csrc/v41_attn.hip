@@ -788,34 +788,44 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
   }
 
   // ---- merge the wavefronts: M = max m_w, O = sum 2^(m_w - M) O_w,
-  // l = sum 2^(m_w - M) l_w
+  // l = sum 2^(m_w - M) l_w.  Each wavefront's half of O goes, unscaled,
+  // into its own slot (free once its last tile is done), so the first half
+  // is written before the barrier, while other wavefronts still work.
   const float l_w = group_sum(l_part);
   if (g == 0) {
     xm[wave][r16] = m2;
     xl[wave][r16] = l_w;
   }
+  static_assert(kHalfDT * kWave * 16 <= WS::kBytes, "half of O fits a slot");
+  // [wave slot][half dim-tile][lane]
+  auto merge_at = [&](int w, int j) -> f32x4* {
+    return reinterpret_cast<f32x4*>(slots + w * WS::kBytes) + j * kWave + lane;
+  };
+#pragma unroll
+  for (int j = 0; j < kHalfDT; ++j) *merge_at(wave, j) = acc_o[j];
   lds_barrier();
   float M = kNegInf;
 #pragma unroll
   for (int w = 0; w < kW; ++w) M = fmaxf(M, xm[w][r16]);
   float l_tot = 0.0f;
+  float wt[kW];  // 2^(m_w - M) of head r16, 0 for a wavefront without rows
 #pragma unroll
   for (int w = 0; w < kW; ++w) {
     const float mw = xm[w][r16];
-    l_tot += (mw == kNegInf) ? 0.0f : xl[w][r16] * exp2f(mw - M);
+    wt[w] = (mw == kNegInf) ? 0.0f : exp2f(mw - M);
+    l_tot += xl[w][r16] * wt[w];
   }
-  const float my_w = (m2 == kNegInf) ? 0.0f : exp2f(m2 - M);
   const float sink_term = (sink2 == kNegInf) ? 0.0f : exp2f(sink2 - M);
   const float den = l_tot + sink_term;
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-  f32x4* const merge = reinterpret_cast<f32x4*>(slots);  // [wave][half dim-tile][lane]
   constexpr int kPerWave = kHalfDT / kW;  // dim-tiles each wavefront finishes per half
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
+    if (h == 1) {
 #pragma unroll
-    for (int j = 0; j < kHalfDT; ++j)
-      merge[(wave * kHalfDT + j) * kWave + lane] = acc_o[h * kHalfDT + j] * my_w;
-    lds_barrier();
+      for (int j = 0; j < kHalfDT; ++j) *merge_at(wave, j) = acc_o[kHalfDT + j];
+      lds_barrier();
+    }
     if (kPerWave > 0 || wave < kHalfDT) {
       const int j0 = kPerWave > 0 ? wave * kPerWave : wave;
       const int jn = kPerWave > 0 ? kPerWave : 1;
@@ -823,7 +833,7 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
         const int j = j0 + jj;
         f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int w = 0; w < kW; ++w) o += merge[(w * kHalfDT + j) * kWave + lane];
+        for (int w = 0; w < kW; ++w) o += *merge_at(w, j) * wt[w];
         const int dim = 16 * (h * kHalfDT + j) + 4 * g;  // lane: dims dim .. dim+3, head r16
         if (!head_ok) continue;
         if (p.splits == 1) {
@@ -837,7 +847,7 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
         }
       }
     }
-    lds_barrier();
+    if (h == 0) lds_barrier();  // every wavefront has read the first half
   }
   if (p.splits > 1 && head_ok && wave == 0 && g == 0) {
     const int64_t slot_i = (qi * p.splits + split) * p.n_heads + head;
