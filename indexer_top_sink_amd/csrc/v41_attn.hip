@@ -1123,18 +1123,41 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   const int d4 = e - h * Q4;
   const float kNegInf = -__builtin_huge_valf();
   const float sink2 = sink[h] * kLog2e;
+  // splits in chunks of kChunk: a chunk's loads are all issued before any
+  // returns, then its maximum updates the running one (a single chunk gives
+  // exactly the two-pass form: M over the sink and every split first)
+  constexpr int kChunk = 8;
   float M = sink2;
-  for (int s = 0; s < splits; ++s)
-    M = fmaxf(M, part_ml[2 * ((qi * splits + s) * n_heads + h)]);
-  float den = (sink2 == kNegInf) ? 0.0f : exp2f(sink2 - M);
+  float den = (sink2 == kNegInf) ? 0.0f : 1.0f;  // 2^(sink - M) at M = sink
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < splits; ++s) {
-    const int64_t slot = (qi * splits + s) * n_heads + h;
-    const float ms = part_ml[2 * slot];
-    const float wgt = (ms == kNegInf) ? 0.0f : exp2f(ms - M);
-    den += part_ml[2 * slot + 1] * wgt;
-    const f32x4 v = *reinterpret_cast<const f32x4*>(part_o + slot * D + 4 * d4);
-    acc += v * wgt;
+  for (int s0 = 0; s0 < splits; s0 += kChunk) {
+    float2 ml[kChunk];
+    f32x4 v[kChunk];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      ml[i] = make_float2(kNegInf, 0.0f);
+      v[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      if (s0 + i < splits) {
+        const int64_t slot = (qi * splits + s0 + i) * n_heads + h;
+        ml[i] = *reinterpret_cast<const float2*>(part_ml + 2 * slot);
+        v[i] = *reinterpret_cast<const f32x4*>(part_o + slot * D + 4 * d4);
+      }
+    }
+    float Mc = M;
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) Mc = fmaxf(Mc, ml[i].x);
+    if (Mc > M) {
+      const float a = (M == kNegInf) ? 0.0f : exp2f(M - Mc);
+      den *= a;
+      acc *= a;
+      M = Mc;
+    }
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      const float wgt = (ml[i].x == kNegInf) ? 0.0f : exp2f(ml[i].x - M);
+      den += ml[i].y * wgt;
+      acc += v[i] * wgt;
+    }
   }
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
   uint2 o;
