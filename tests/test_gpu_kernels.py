@@ -321,6 +321,7 @@ def oracle_attn(q, rows_a, rows_b, idx, sink, scale, B, T):
     (2, 1, 40, 512, 128, 300, 640, True),      # one round per split, a partial head group
     (1, 200, 70, 512, 64, 100, 64, True),      # wide form at 512 dims, a 6-head second group
     (1, 1, 64, 512, 128, 4000, 2048, True),    # widest row: 16 splits of one round each
+    (1, 1, 64, 512, 128, 3000, 1536, True),    # 12 splits: a full and a partial combine chunk
     (2, 1, 64, 512, 128, 3000, 2048, False),   # widest row unsplit: 16 tiles per wavefront
     (1, 256, 64, 64, 256, 3000, 2048, True),   # widest row in the wide form (compacted list)
 ])
@@ -354,10 +355,11 @@ def test_attn_all_absent_and_one_row(v41):
     assert_attn_close(got, want, "one row")
 
 
-@pytest.mark.parametrize("A", [300, 120])
+@pytest.mark.parametrize("A", [300, 120, 1200])
 def test_attn_large_logits(v41, A):
     """Scores far from zero exercise the running max (no overflow); 300 rows
-    take two rounds per split (wavefronts merged at the end), 120 one round."""
+    take two rounds per split (wavefronts merged at the end), 120 one round,
+    1200 nine splits (the combine's running max across two chunks)."""
     H, D = 64, 512
     rng = np.random.default_rng(4)
     q = bf16_of(rng.standard_normal((1, H, D)) * 4)
