@@ -208,9 +208,8 @@ int v41_candidate_blocks(const float *scores, int64_t n_sel_rows, int64_t n_cols
  *           f32 rounding order.  Calls that share a workspace must not
  *           overlap in time.
  * QK^T and PV run as bf16 products with f32 accumulation; the softmax is in
- * f32; the probabilities enter PV rounded to bf16 (for head_dim 512 with at
- * most 128 rows per workgroup, as a pair of bf16 terms: high part plus
- * remainder).
+ * f32; the probabilities enter PV as a pair of bf16 terms (high part plus
+ * remainder), about 16 significant bits.
  */
 int v41_sparse_attn_sink(const v41_bf16 *q, const v41_bf16 *rows_a,
                          int64_t rows_a_len, int64_t a_bs,

@@ -25,8 +25,9 @@
 //  * O^T += G^T P^T: the A operand (16 dims x 32 rows) comes from the same
 //    row-major tile through two ds_read_b64_tr_b16 transposing loads, and the
 //    B operand is the probabilities exactly as the S^T accumulator left them
-//    in the lane (the transposing loads fetch the rows in that order), rounded
-//    to bf16.
+//    in the lane (the transposing loads fetch the rows in that order), as a
+//    pair of bf16 terms (high part and remainder, two products per operand
+//    read), so P enters the product with about 16 significant bits.
 // When even the narrow grid does not cover the compute units, a query's rows
 // are split over several workgroups, each writing an f32 partial (max, sum,
 // O), and a combine kernel merges them.
@@ -408,13 +409,17 @@ __global__ __launch_bounds__(kThreads, NS == 2 ? 2 : 1) void attn_kernel(Params 
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc_o[mt] *= alpha;
     }
-    bf16x8 pf;
+    // probabilities as a bf16 pair (high part and remainder): P enters the
+    // product with about 16 significant bits
+    bf16x8 pf, pr;
     float psum = 0.0f;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const float pv = (sv[s] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(sv[s] - m2);
       psum += pv;
-      pf[s] = (__bf16)pv;
+      const __bf16 h = (__bf16)pv;
+      pf[s] = h;
+      pr[s] = (__bf16)(pv - (float)h);
     }
     l_part += psum;
     // O^T += G^T P^T, four M-tiles per batch of transposing loads
@@ -428,6 +433,11 @@ __global__ __launch_bounds__(kThreads, NS == 2 ? 2 : 1) void attn_kernel(Params 
       for (int j = 0; j < 4; ++j) {
         const u32x4 a = {t[2 * j][0], t[2 * j][1], t[2 * j + 1][0], t[2 * j + 1][1]};
         acc_o[mt0 + j] = mfma16x16x32(as_bf16x8(a), pf, acc_o[mt0 + j]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4 a = {t[2 * j][0], t[2 * j][1], t[2 * j + 1][0], t[2 * j + 1][1]};
+        acc_o[mt0 + j] = mfma16x16x32(as_bf16x8(a), pr, acc_o[mt0 + j]);
       }
     }
   }
@@ -516,7 +526,8 @@ __global__ __launch_bounds__(kThreads, NS == 2 ? 2 : 1) void attn_kernel(Params 
 //    the A operand of O^T += G^T P^T, all D dims;
 //  * QK: 16 rows x 16 heads over four independent accumulators; the S
 //    accumulator is laid out as the B operand of a 16x16x16 PV product, so
-//    the bf16 probabilities never leave the lane;
+//    the probabilities (a bf16 high part and remainder, one product each)
+//    never leave the lane;
 //  * head maxima and sums across the lane groups use permlane swaps;
 //  * no barrier inside the loop; at the end the eight (max, sum, O) are
 //    merged through LDS, half of the dims at a time.
@@ -758,15 +769,19 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) acc_o[dt] *= alpha;
     }
-    u32x2 pk;
+    // probabilities as a bf16 pair (high part pk and remainder pl)
+    u32x2 pk, pl;
 #pragma unroll
     for (int e = 0; e < 4; e += 2) {
       const float p0 = (sv[e] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(sv[e] - m2);
       const float p1 = (sv[e + 1] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(sv[e + 1] - m2);
       l_part += p0 + p1;
       const __bf16 b0 = (__bf16)p0, b1 = (__bf16)p1;
+      const __bf16 c0 = (__bf16)(p0 - (float)b0), c1 = (__bf16)(p1 - (float)b1);
       pk[e / 2] = (uint32_t)__builtin_bit_cast(uint16_t, b0) |
                   ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+      pl[e / 2] = (uint32_t)__builtin_bit_cast(uint16_t, c0) |
+                  ((uint32_t)__builtin_bit_cast(uint16_t, c1) << 16);
     }
     // O^T[dims][head] += G^T[dims][16 rows] P^T[16 rows][head]
     if constexpr (DT >= 8) {
@@ -776,12 +791,16 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
         tr_load8(t, tr_addr + 32 * d0);
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc_o[d0 + j] = mfma16x16x16(t[j], pk, acc_o[d0 + j]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc_o[d0 + j] = mfma16x16x16(t[j], pl, acc_o[d0 + j]);
       }
     } else {
       u32x2 t[4];
       tr_load4_1(t, tr_addr);
 #pragma unroll
       for (int j = 0; j < DT; ++j) acc_o[j] = mfma16x16x16(t[j], pk, acc_o[j]);
+#pragma unroll
+      for (int j = 0; j < DT; ++j) acc_o[j] = mfma16x16x16(t[j], pl, acc_o[j]);
     }
     cur = nxt;
     vm_cur = vm_nxt;

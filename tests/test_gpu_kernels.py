@@ -355,17 +355,38 @@ def test_attn_all_absent_and_one_row(v41):
     assert_attn_close(got, want, "one row")
 
 
+@pytest.mark.parametrize("seed", range(4, 12))
 @pytest.mark.parametrize("A", [300, 120, 1200])
-def test_attn_large_logits(v41, A):
-    """Scores far from zero exercise the running max (no overflow); 300 rows
-    take two rounds per split (wavefronts merged at the end), 120 one round,
-    1200 nine splits (the combine's running max across two chunks)."""
+def test_attn_large_logits(v41, A, seed):
+    """Scores far from zero (logits of standard deviation about 16, rows up to
+    about 16 in size) exercise the running max (no overflow) and the
+    precision of the probabilities in PV; 300 rows take two rounds per split
+    (wavefronts merged at the end), 120 one round, 1200 nine splits (the
+    combine's running max across two chunks)."""
     H, D = 64, 512
-    rng = np.random.default_rng(4)
+    rng = np.random.default_rng(seed)
     q = bf16_of(rng.standard_normal((1, H, D)) * 4)
     rows_a = bf16_of(rng.standard_normal((1, A, D)) * 4)
     idx = rng.permutation(A)[None, :].astype(np.int32)
     sink = (rng.standard_normal(H) * 30).astype(np.float32)
     got = run_attn(v41, q, rows_a, None, idx, sink, 0.044194173, 1, 1)
     want = oracle_attn(q, rows_a, None, idx, sink, 0.044194173, 1, 1)
-    assert_attn_close(got, want, "large logits")
+    r = assert_attn_close(got, want, f"large logits A={A} seed={seed}")
+    assert r["frac_within_2ulp"] >= 0.999, r
+
+
+@pytest.mark.parametrize("seed", [4, 5])
+def test_attn_large_logits_wide(v41, seed):
+    """The same stress on the wide form (256 queries, so one workgroup per
+    query and 64 heads): 120 rows, a few of them dominant per head."""
+    T, H, D, A = 256, 64, 512, 120
+    rng = np.random.default_rng(100 + seed)
+    q = bf16_of(rng.standard_normal((T, H, D)) * 4)
+    rows_a = bf16_of(rng.standard_normal((1, A, D)) * 4)
+    idx = np.stack([rng.permutation(A) for _ in range(T)]).astype(np.int32)
+    idx[rng.uniform(size=idx.shape) < 0.3] = -1
+    sink = (rng.standard_normal(H) * 30).astype(np.float32)
+    got = run_attn(v41, q, rows_a, None, idx, sink, 0.044194173, 1, T)
+    want = oracle_attn(q, rows_a, None, idx, sink, 0.044194173, 1, T)
+    r = assert_attn_close(got, want, f"large logits wide seed={seed}")
+    assert r["frac_within_2ulp"] >= 0.999, r
