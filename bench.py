@@ -5,17 +5,31 @@ indices, indexer scores, top-k, sparse attention with the sink) over one batch
 of synthetic input already resident in HBM.  The default workload is the
 batched decode: 64 sequences at context 32768 (8192 compressed rows each),
 64 heads x 512, window 128, indexer 64 x 128, top-512; a step decodes one
-token per sequence.  The prefill chunk (2048 tokens at position 0) is
-reported alongside.
+token per sequence.  The prefill chunk (2048 tokens at position 0), the
+long-context decode (16 sequences at context 131072 with planted ties) and one
+sequence at context 4096 (latency) are reported alongside.
 
-A decode step is one v41_decode_step call (four launches, positions read on
-the device); the same step as the five separate calls is timed alongside
-(--separate-calls makes that form the headline).  Input staging rotates several
-copies of every input tensor, so a step never reads what the previous step left
-in the 256 MB last-level cache (as in a model, where the other layers run in
-between).  Each step is captured once in a HIP graph per copy and replayed; per-kernel durations come from HIP events
-around graph replays of single kernels on the same stream.  The CPU baseline
-is the oracle (plain C, one thread) on a bounded sample of the same workload.
+A decode step is one v41_decode_step call (three or four launches, positions
+read on the device); the same step as the five separate calls is timed
+alongside (--separate-calls makes that form the headline).
+
+Timing.  Every input tensor exists in several copies (input sets); step i
+runs on set i mod n, so a set's data was last touched n - 1 steps earlier
+(for the decode workloads more than the 256 MB last-level cache in between).
+One HIP graph holds one step per set and is replayed, with an event after
+each replay: the value is K over the first-to-last event time, and the
+replays give the median and 90th percentile of the per-step time.  Per
+kernel: each rep reads a 1 GiB buffer that evicts the last-level cache, then
+launches the kernel once on each input set, directly, between two events, so
+every launch reads its data from HBM; mean, p50 and p90 over the reps of the
+per-launch time.  Rooflines use the mean.
+Fractions are given against the published peaks and against ceilings measured
+in the same run (a 1 GiB device copy; an 8192^3 bf16 torch.mm).
+
+The CPU baseline is the oracle (plain C), run before the GPU is touched: one
+thread on a bounded sample, and a process pool over the step's sequences
+(tokens) on the host cores available (at most 16), with the core count and
+CPU model.
 
 With --rope the step starts from q and kv rows before their rotation: q is
 rotated in place and the fp8 call becomes the fused rotation + fp8 + ring write
@@ -223,6 +237,103 @@ def time_replays(graphs, reps, torch):
     return e0.elapsed_time(e1) / reps
 
 
+def stats(xs):
+    """mean, median and 90th percentile of a list of times."""
+    a = np.asarray(xs, dtype=np.float64)
+    return {"mean": float(a.mean()), "p50": float(np.percentile(a, 50)),
+            "p90": float(np.percentile(a, 90))}
+
+
+class CacheEvictor:
+    """Reads a 1 GiB buffer (four times the 256 MB last-level cache): after it
+    the cache holds only clean lines of this buffer, so the next kernel's
+    data comes from HBM and no dirty line of earlier work is written back
+    inside the timed region.  It also keeps the GPU busy long enough for the
+    host to queue the timed launches behind it."""
+
+    def __init__(self, torch, device, mib=1024):
+        self.buf = torch.ones(mib << 18, dtype=torch.float32, device=device)
+        self.sink = torch.empty((), dtype=torch.float32, device=device)
+
+    def __call__(self, torch):
+        torch.sum(self.buf, dim=0, out=self.sink)
+
+
+def time_kernel(fns, reps, evict, torch):
+    """Per-launch ms of one kernel: fns launch it once on each input set.
+    Every rep evicts the last-level cache, then launches fns directly (no
+    graph: the launches queue up behind the eviction, so they run back to
+    back) between two events; returns mean, p50 and p90 over the reps of
+    the per-launch average."""
+    st = torch.cuda.current_stream()
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for e0, e1 in ev:
+        evict(torch)
+        e0.record(st)
+        for f in fns:
+            f()
+        e1.record(st)
+    torch.cuda.synchronize()
+    return stats([e0.elapsed_time(e1) / len(fns) for e0, e1 in ev])
+
+
+def measured_ceilings(torch, device):
+    """What this GPU reaches on plain work, for fractions beside the
+    published peaks (best of 5 each):
+      hbm_GBs        the library's read probe over 2 GiB, non-temporal loads
+                     (the decode kernels mostly read);
+      hbm_copy_GBs   a 2 GiB torch device copy, bytes read + written;
+      mfma_bf16_TFLOPs  the library's matrix-core probe: independent
+                     v_mfma_f32_16x16x32_bf16 chains on registers, 512
+                     workgroups of four wavefronts, about 1 ms;
+      gemm_bf16_TFLOPs  an 8192^3 bf16 torch.mm (a library GEMM)."""
+    from indexer_top_sink_amd import v41
+    n = 2 << 30
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def best(fn):
+        fn()
+        t = 1e30
+        for _ in range(5):
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            t = min(t, e0.elapsed_time(e1))
+        return t
+
+    src = torch.ones(n // 4, dtype=torch.float32, device=device)
+    sink = torch.zeros(4, dtype=torch.int32, device=device)
+    t_read = best(lambda: v41.v41_probe_hbm_read(src, n, 1, sink))
+    t_read_c = best(lambda: v41.v41_probe_hbm_read(src, n, 0, sink))
+    dst = torch.empty_like(src)
+    t_copy = best(lambda: dst.copy_(src))
+    del src, dst
+    wgs, iters = 512, 8000
+    fsink = torch.zeros(4, dtype=torch.float32, device=device)
+    t_mfma = best(lambda: v41.v41_probe_mfma(wgs, iters, fsink))
+    m = 8192
+    a = torch.randn(m, m, dtype=torch.bfloat16, device=device)
+    b = torch.randn(m, m, dtype=torch.bfloat16, device=device)
+    c = torch.empty(m, m, dtype=torch.bfloat16, device=device)
+    t_mm = best(lambda: torch.mm(a, b, out=c))
+    del a, b, c
+    torch.cuda.synchronize()
+    return {"hbm_GBs": round(n / (t_read * 1e-3) / 1e9, 1),
+            "hbm_cached_loads_GBs": round(n / (t_read_c * 1e-3) / 1e9, 1),
+            "hbm_copy_GBs": round(2 * n / (t_copy * 1e-3) / 1e9, 1),
+            "mfma_bf16_TFLOPs": round(524288 * wgs * iters / (t_mfma * 1e-3) / 1e12, 1),
+            "gemm_bf16_TFLOPs": round(2 * m ** 3 / (t_mm * 1e-3) / 1e12, 1),
+            "how": "hbm: v41_probe_hbm_read over 2 GiB (non-temporal, and default loads); "
+                   "copy: 2 GiB torch copy (read + write bytes); mfma: v41_probe_mfma "
+                   "(512 x 4 wavefronts x 8000 x 8 independent 16x16x32 bf16); gemm: 8192^3 "
+                   "bf16 torch.mm; best of 5 each"}
+
+
 # ----------------------------------------------------------------- algorithmic work
 def algorithmic(wl, host_idx=None, valid_pairs=None, rope=False):
     """Bytes and flops per kernel of one step (what the method must move or
@@ -332,64 +443,134 @@ def time_grouped_output(torch, device, steps, n_tokens):
 
 
 # ----------------------------------------------------------------- CPU baseline
-def cpu_baseline(wl, n_sample, budget_s=30.0):
-    """The oracle (plain C, one thread) on the first sequences / tokens of the
-    same workload; tokens per second scaled from the sample."""
+def _oracle_decode(job):
+    """Worker: the oracle's decode step for each listed sequence; returns
+    (sequences done, seconds inside the oracle)."""
     import oracle as O
     from oracle import layer as OL
+    name, seqs = job
+    wl = WL.WORKLOADS[name]
     sink = WL.layer_sink(wl)
-    t_total = 0.0
-    done = 0
-    if wl.mode == "decode":
-        for b in range(n_sample):
-            d = WL.decode_sequence(wl, b)
-            ring = O.WindowCache(wl.window, wl.head_dim)
-            ring.rows[:] = O.fp8_round_rows(d["ring_raw"])
-            t0 = time.perf_counter()
-            OL.decode(ring, d["kv_new"], wl.start_pos, d["q"], sink, wl.scale, ratio=wl.ratio,
-                      latent=d["latent"], kI=d["kI"], qI=d["qI"], w=d["w"], k=wl.topk)
-            t_total += time.perf_counter() - t0
-            done += 1
-            if t_total > budget_s:
-                break
-        sample = f"{done} of {wl.batch} sequences, one decode step each"
-    else:
-        d = WL.prefill_inputs(wl)
-        toks = list(range(wl.n_tokens - n_sample, wl.n_tokens))   # the costliest tokens
+    busy = 0.0
+    for b in seqs:
+        d = WL.decode_sequence(wl, b)
+        ring = O.WindowCache(wl.window, wl.head_dim)
+        ring.rows[:] = O.fp8_round_rows(d["ring_raw"])
         t0 = time.perf_counter()
-        OL.prefill(d["kv_chunk"], d["q"], sink, wl.scale, wl.window, ratio=wl.ratio,
-                   latent=d["latent"], kI=d["kI"], qI=d["qI"], w=d["w"], cand=d["cand"],
-                   cand_block=wl.cand_block, k=wl.topk, queries=toks)
-        t_total = time.perf_counter() - t0
-        done = len(toks)
-        sample = f"the last {done} of {wl.n_tokens} prefill tokens (the longest rows)"
-    return {"value": done / t_total, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": sample, "seconds": round(t_total, 3)}
+        OL.decode(ring, d["kv_new"], wl.start_pos, d["q"], sink, wl.scale, ratio=wl.ratio,
+                  latent=d["latent"], kI=d["kI"], qI=d["qI"], w=d["w"], k=wl.topk)
+        busy += time.perf_counter() - t0
+    return len(seqs), busy
+
+
+def _oracle_prefill(job):
+    """Worker: the oracle's prefill chunk over the listed tokens."""
+    from oracle import layer as OL
+    name, toks = job
+    wl = WL.WORKLOADS[name]
+    d = WL.prefill_inputs(wl)
+    t0 = time.perf_counter()
+    OL.prefill(d["kv_chunk"], d["q"], WL.layer_sink(wl), wl.scale, wl.window, ratio=wl.ratio,
+               latent=d["latent"], kI=d["kI"], qI=d["qI"], w=d["w"], cand=d["cand"],
+               cand_block=wl.cand_block, k=wl.topk, queries=list(toks))
+    return len(toks), time.perf_counter() - t0
+
+
+def host_cpu():
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return model, os.cpu_count() or 1, avail
+
+
+def cpu_baseline(wl, budget_s=10.0, max_workers=16):
+    """The oracle (plain C, double precision), as it stands, on the host cores,
+    two ways: one thread on the first sequences (tokens) of the workload until
+    about budget_s of oracle time, and a process pool over independent
+    sequences (tokens), one worker per available core up to max_workers (the
+    host share of one GPU), whose throughput is the work done over the
+    busiest worker's oracle time.  Runs before this process touches the GPU,
+    so the pool's fork is safe."""
+    import multiprocessing as mp
+    model, nproc, avail = host_cpu()
+    workers = max(1, min(max_workers, avail))
+    if wl.mode == "decode":
+        done, busy = 0, 0.0
+        while done < wl.batch and busy < budget_s:
+            n, t = _oracle_decode((wl.name, [done]))
+            done += n
+            busy += t
+        single = {"value": done / busy, "seconds": round(busy, 3),
+                  "sample": f"{done} of {wl.batch} sequences, one decode step each"}
+        chunks = [list(range(wl.batch))[i::workers] for i in range(workers)]
+        jobs = [(wl.name, c) for c in chunks if c]
+        fn = _oracle_decode
+        unit_name = "sequences"
+    else:
+        toks = list(range(wl.n_tokens - 16, wl.n_tokens))    # the costliest tokens
+        n, t = _oracle_prefill((wl.name, toks))
+        single = {"value": n / t, "seconds": round(t, 3),
+                  "sample": f"the last {n} of {wl.n_tokens} prefill tokens (the longest rows)"}
+        span = list(range(wl.n_tokens - 16 * workers, wl.n_tokens))
+        jobs = [(wl.name, span[i::workers]) for i in range(workers)]
+        fn = _oracle_prefill
+        unit_name = "tokens"
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(len(jobs)) as pool:
+        res = pool.map(fn, jobs)
+    wall = time.perf_counter() - t0
+    n_all = sum(n for n, _ in res)
+    busiest = max(t for _, t in res)
+    return {"value": round(n_all / busiest, 3), "unit": "tokens/s", "cores": len(jobs),
+            "kind": "oracle",
+            "sample": f"{n_all} {unit_name} of one step over {len(jobs)} worker processes "
+                      f"(throughput = work / busiest worker's oracle seconds)",
+            "seconds": round(busiest, 3), "pool_wall_s": round(wall, 3),
+            "single_thread": {**{k: (round(v, 3) if isinstance(v, float) else v)
+                                 for k, v in single.items()}, "unit": "tokens/s",
+                              "cores": 1},
+            "cpu_model": model, "nproc": nproc, "cores_available": avail}
 
 
 # ----------------------------------------------------------------- main
 def timed_steps(step_fns, steps, warmup, torch):
-    """Mean ms per step: one graph holds one step per input set (as one graph
-    would hold the layers of a model), single-step graphs cover a remainder
-    of K; W warm-up steps first."""
-    n_sets = len(step_fns)
+    """K steps: replays of one HIP graph that holds one step per input set
+    (n steps per replay, as one graph would hold a model's layers), with an
+    event after each replay, plus single-step graphs for a remainder of K.
+    Returns the mean ms per step over all K (first event to last), the
+    mean/p50/p90 over the full replays of the per-step time, and the
+    single-step graphs.  W warm-up steps first."""
+    n = len(step_fns)
     all_graph = capture([f for c in step_fns for f in c], torch)
     one_graphs = [capture(c, torch) for c in step_fns]
-    for i in range(max(1, warmup // n_sets)):
+    for _ in range(max(1, warmup // n)):
         all_graph.replay()
     torch.cuda.synchronize()
     st = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    full, rest = divmod(steps, n_sets)
-    torch.cuda.synchronize()
-    e0.record(st)
-    for _ in range(full):
+    full, rest = divmod(steps, n)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(full + 2)]
+    ev[0].record(st)
+    for i in range(full):
         all_graph.replay()
+        ev[i + 1].record(st)
     for i in range(rest):
         one_graphs[i].replay()
-    e1.record(st)
-    e1.synchronize()
-    return e0.elapsed_time(e1) / steps, one_graphs
+    ev[-1].record(st)
+    ev[-1].synchronize()
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) / n for i in range(full)] or \
+        [ev[0].elapsed_time(ev[-1]) / steps]
+    return ev[0].elapsed_time(ev[-1]) / steps, stats(per), one_graphs
 
 
 def fused_call(buf, rope):
@@ -400,11 +581,12 @@ def fused_call(buf, rope):
     return lambda: v41.v41_decode_step(args)
 
 
-def run_workload(name, steps, warmup, n_sets, torch, device, rope=False, separate=False):
+def run_workload(name, steps, warmup, n_sets, torch, device, evict, rope=False,
+                 separate=False):
     """Times K steps of a workload.  A decode step is one v41_decode_step call
-    (unless separate); its separate-call form is timed alongside.  Returns
-    (workload, ms per step, per-kernel us, algorithmic work, ms per step of
-    the separate calls or None)."""
+    (unless separate); its separate-call form is timed alongside.  Per-kernel
+    times: each kernel launched once on each input set in one graph, every
+    replay after a cache eviction.  Returns a dict."""
     wl = WL.WORKLOADS[name]
     t0 = time.time()
     if wl.mode == "decode":
@@ -422,28 +604,24 @@ def run_workload(name, steps, warmup, n_sets, torch, device, rope=False, separat
 
     calls = [step_calls(s, wl.mode, rope) for s in sets]
     sep_fns = [[f for _, f in c] for c in calls]
-    ms_sep = None
+    ms_sep = sep_stats = None
     if wl.mode == "decode" and not separate:
-        ms_step, one_graphs = timed_steps([[fused_call(s, rope)] for s in sets], steps, warmup,
-                                          torch)
-        ms_sep, _ = timed_steps(sep_fns, steps, warmup, torch)
+        ms_step, st_stats, graphs = timed_steps([[fused_call(s, rope)] for s in sets], steps,
+                                                warmup, torch)
+        ms_sep, sep_stats, _ = timed_steps(sep_fns, steps, warmup, torch)
         log(f"{name}{' + rope' if rope else ''}: {ms_step * 1e3:.1f} us per step "
             f"({ms_sep * 1e3:.1f} us as separate calls)")
     else:
-        ms_step, one_graphs = timed_steps(sep_fns, steps, warmup, torch)
+        ms_step, st_stats, graphs = timed_steps(sep_fns, steps, warmup, torch)
         log(f"{name}{' + rope' if rope else ''}: {ms_step * 1e3:.1f} us per step")
 
-    # per-kernel durations: a graph of 4 * n_sets launches of one kernel
-    # cycling over the input sets, replayed; mean time per launch
-    kern_us = {}
-    per_graph = 4 * n_sets
+    kern = {}
+    reps = max(10, steps // 2)
     for ki, (kname, _) in enumerate(calls[0]):
-        g = capture([calls[i % n_sets][ki][1] for i in range(per_graph)], torch)
-        g.replay()
-        reps = max(4, steps // per_graph)
-        kern_us[kname] = time_replays([g], reps, torch) * 1e3 / per_graph
+        fns = [calls[i][ki][1] for i in range(n_sets)]
+        kern[kname] = {k: v * 1e3 for k, v in time_kernel(fns, reps, evict, torch).items()}
     # restore a consistent state (the index buffer is rebuilt by a full step)
-    one_graphs[0].replay()
+    graphs[0].replay()
     torch.cuda.synchronize()
 
     idx = sets[0].idx.cpu().numpy()
@@ -456,7 +634,10 @@ def run_workload(name, steps, warmup, n_sets, torch, device, rope=False, separat
             blocks = np.repeat(cand[t].astype(bool), wl.cand_block)[:n]
             pairs += int(blocks.sum())
     work = algorithmic(wl, host_idx=idx, valid_pairs=pairs, rope=rope)
-    return wl, ms_step, kern_us, work, ms_sep
+    del sets, calls, sep_fns, graphs
+    torch.cuda.empty_cache()
+    return {"wl": wl, "ms_step": ms_step, "step_stats": st_stats, "kern": kern, "work": work,
+            "ms_sep": ms_sep, "sep_stats": sep_stats}
 
 
 # Sources of each kernel: a stored traffic figure holds only while they are
@@ -493,19 +674,56 @@ def measured_traffic(kname, workload):
     return None
 
 
-def roofline_entry(kname, work, us, bound, workload=None):
+def roofline_entry(kname, work, kt, bound, workload=None, ceilings=None):
+    """Roofline of one kernel: algorithmic bytes (flops) per launch over its
+    mean launch time; kt holds the mean / p50 / p90 launch times in us."""
     w = work[kname]
+    us = kt["mean"]
     if bound == "hbm":
         achieved = w["bytes"] / (us * 1e-6) / 1e9
         peak, unit = HBM_PEAK_GBS, "GB/s"
+        measured = ceilings.get("hbm_GBs") if ceilings else None
     else:
         achieved = w["flops"] / (us * 1e-6) / 1e12
         peak, unit = BF16_PEAK_TFLOPS, "TFLOP/s"
+        measured = ceilings.get("mfma_bf16_TFLOPs") if ceilings else None
     traffic = measured_traffic(kname, workload) if workload else None
     return {"kernel": kname, "bound": bound, "achieved": round(achieved, 1), "peak": peak,
             "unit": unit, "frac": round(achieved / peak, 4), "traffic": traffic,
-            "avg_us": round(us, 2), "algorithmic_bytes": w["bytes"],
-            "algorithmic_flops": w["flops"]}
+            "frac_of_measured": round(achieved / measured, 4) if measured else None,
+            "avg_us": round(us, 2), "p50_us": round(kt["p50"], 2), "p90_us": round(kt["p90"], 2),
+            "algorithmic_bytes": w["bytes"], "algorithmic_flops": w["flops"]}
+
+
+def us_stats(st):
+    return {k: round(v * 1e3, 2) for k, v in st.items()}
+
+
+def decode_summary(r, ceilings):
+    """A decode workload's line: throughput, step time distribution, and the
+    roofline of each timed kernel (the longest as `roofline`)."""
+    wl, kern, work = r["wl"], r["kern"], r["work"]
+    dominant = max(kern, key=lambda k: kern[k]["mean"])
+    return {
+        "value": round(wl.queries / (r["ms_step"] * 1e-3), 1), "unit": "tokens/s",
+        "ms_per_step": round(r["ms_step"], 5), "step_us": us_stats(r["step_stats"]),
+        "roofline": roofline_entry(dominant, work, kern[dominant], "hbm", wl.name, ceilings),
+        "kernels": {k: roofline_entry(k, work, kern[k], "hbm", wl.name, ceilings)
+                    for k in kern},
+        "path_hbm_frac": path_frac(r),
+        "ms_per_step_separate_calls": (round(r["ms_sep"], 5) if r["ms_sep"] is not None
+                                       else None)}
+
+
+def path_frac(r):
+    """Indexer + attention together: their algorithmic bytes over their summed
+    mean launch times, as a fraction of the published HBM peak."""
+    k, w = r["kern"], r["work"]
+    names = [n for n in ("indexer_scores", "sparse_attn_sink") if n in k]
+    nbytes = sum(w[n]["bytes"] for n in names)
+    us = sum(k[n]["mean"] for n in names)
+    return {"kernels": names, "bytes": nbytes, "us": round(us, 2),
+            "frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def main():
@@ -514,7 +732,7 @@ def main():
     ap.add_argument("--steps", type=int, default=48)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode64", choices=sorted(WL.WORKLOADS))
-    ap.add_argument("--input-sets", type=int, default=3)
+    ap.add_argument("--input-sets", type=int, default=4)
     ap.add_argument("--rope", action="store_true",
                     help="make the rotary epilogue (q rotation; kv rotation + fp8 + ring "
                          "write) part of the timed step")
@@ -526,7 +744,6 @@ def main():
                          "and prefill sizes and print that as the JSON line")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
                     help="first copy MB megabytes device to device three times (the "
                          "known-size kernel that scales HBM byte counters)")
@@ -536,6 +753,15 @@ def main():
               "take its own shard of sequences or tokens with no exchange, so run one "
               "process per GPU", file=sys.stderr)
         sys.exit(2)
+    wl = WL.WORKLOADS[args.workload]
+
+    # the oracle first, before anything touches the GPU (its pool forks)
+    cpu = None
+    if not args.no_cpu_baseline and not args.output_side:
+        t0 = time.time()
+        cpu = cpu_baseline(wl)
+        log(f"cpu baseline in {time.time() - t0:.1f}s: {cpu['value']:.2f} tokens/s on "
+            f"{cpu['cores']} processes, {cpu['single_thread']['value']:.2f} on one thread")
 
     import torch
     device = torch.device("cuda:0")
@@ -560,19 +786,21 @@ def main():
                           "higher_is_better": False, "data": "synthetic", "detail": res}),
               flush=True)
         return
-    wl, ms_step, kern_us, work, ms_sep = run_workload(args.workload, args.steps, args.warmup,
-                                                      args.input_sets, torch, device,
-                                                      rope=args.rope,
-                                                      separate=args.separate_calls)
+    ceilings = measured_ceilings(torch, device)
+    log(f"measured ceilings: {ceilings}")
+    evict = CacheEvictor(torch, device)
+    r = run_workload(args.workload, args.steps, args.warmup, args.input_sets, torch, device,
+                     evict, rope=args.rope, separate=args.separate_calls)
+    kern, work, ms_step = r["kern"], r["work"], r["ms_step"]
     tokens = wl.queries
     value = tokens / (ms_step * 1e-3)
     # the dominant kernel is the one that takes the most time; decode moves
     # bytes (HBM bound), a prefill chunk multiplies (MFMA bound)
-    dominant = max(kern_us, key=lambda k: kern_us[k])
+    dominant = max(kern, key=lambda k: kern[k]["mean"])
     bound = "mfma" if wl.mode == "prefill" else "hbm"
-    roof = roofline_entry(dominant, work, kern_us[dominant], bound, wl.name)
-    others = {k: roofline_entry(k, work, kern_us[k], bound, wl.name)
-              for k in ("indexer_scores", "sparse_attn_sink") if k != dominant}
+    roof = roofline_entry(dominant, work, kern[dominant], bound, wl.name, ceilings)
+    others = {k: roofline_entry(k, work, kern[k], bound, wl.name, ceilings)
+              for k in kern if k != dominant}
 
     step_bytes = sum(v["bytes"] for v in work.values())
     out = {
@@ -588,58 +816,69 @@ def main():
                    "topk": wl.topk, "ratio": wl.ratio, "hip_graph": True,
                    "input_sets": args.input_sets, "rope_epilogue": bool(args.rope),
                    "step_form": ("separate calls" if args.separate_calls or wl.mode != "decode"
-                                 else "v41_decode_step")},
+                                 else "v41_decode_step"),
+                   "kernel_timing": "each kernel launched once per input set, back to back, "
+                                    "after a 1 GiB read that evicts the 256 MB last-level "
+                                    "cache; events around the launches"},
+        "step_us": us_stats(r["step_stats"]),
         "roofline": roof,
         "roofline_other": others,
+        "measured_ceilings": ceilings,
         "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "ms_per_step_separate_calls": round(ms_sep, 5) if ms_sep is not None else None,
-        "kernels_us": {k: round(v, 2) for k, v in kern_us.items()},
+        "ms_per_step_separate_calls": round(r["ms_sep"], 5) if r["ms_sep"] is not None else None,
+        "kernels_us": {k: round(v["mean"], 2) for k, v in kern.items()},
     }
+    if wl.mode == "decode":
+        out["path_hbm_frac"] = path_frac(r)
+    sec = out.setdefault("secondary", {}) if not args.no_secondary else {}
     if not args.no_secondary and wl.name != "prefill":
-        pw, pms, pk, pwork, _ = run_workload("prefill", max(12, args.steps // 2), 3,
-                                             args.input_sets, torch, device)
-        out["secondary"] = {
-            "prefill": {
-                "value": round(pw.n_tokens / (pms * 1e-3), 1), "unit": "tokens/s",
-                "ms_per_step": round(pms, 5),
-                "roofline": roofline_entry("sparse_attn_sink", pwork, pk["sparse_attn_sink"],
-                                           "mfma", pw.name),
-                "indexer_roofline": roofline_entry("indexer_scores", pwork,
-                                                   pk["indexer_scores"], "mfma", pw.name),
-                "kernels_us": {k: round(v, 2) for k, v in pk.items()}}}
+        p = run_workload("prefill", max(12, args.steps // 2), 3, args.input_sets, torch, device,
+                         evict)
+        pw, pk, pwork = p["wl"], p["kern"], p["work"]
+        sec["prefill"] = {
+            "value": round(pw.n_tokens / (p["ms_step"] * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(p["ms_step"], 5), "step_us": us_stats(p["step_stats"]),
+            "roofline": roofline_entry("sparse_attn_sink", pwork, pk["sparse_attn_sink"],
+                                       "mfma", pw.name, ceilings),
+            "indexer_roofline": roofline_entry("indexer_scores", pwork, pk["indexer_scores"],
+                                               "mfma", pw.name, ceilings),
+            "kernels_us": {k: round(v["mean"], 2) for k, v in pk.items()}}
+    if not args.no_secondary and wl.name != "decode16":
+        # 16 sequences at context 131072 with the planted ties
+        d = run_workload("decode16", args.steps, args.warmup, args.input_sets, torch, device,
+                         evict, separate=args.separate_calls)
+        sec["decode16"] = decode_summary(d, ceilings)
     if not args.no_secondary and wl.name != "decode1":
-        # one sequence at context 4096: the step's latency floor
-        lw, lms, lk, _, lsep = run_workload("decode1", args.steps, args.warmup,
-                                            args.input_sets, torch, device,
-                                            separate=args.separate_calls)
-        out.setdefault("secondary", {})["decode1_latency"] = {
-            "us_per_step": round(lms * 1e3, 2),
-            "us_per_step_separate_calls": round(lsep * 1e3, 2) if lsep is not None else None,
-            "kernels_us": {k: round(v, 2) for k, v in lk.items()}}
+        # one sequence at context 4096: the step's latency floor (its 1 MB of
+        # data stays in the last-level cache between steps)
+        l = run_workload("decode1", args.steps, args.warmup, args.input_sets, torch, device,
+                         evict, separate=args.separate_calls)
+        sec["decode1_latency"] = {
+            "us_per_step": round(l["ms_step"] * 1e3, 2), "step_us": us_stats(l["step_stats"]),
+            "us_per_step_separate_calls": (round(l["ms_sep"] * 1e3, 2)
+                                           if l["ms_sep"] is not None else None),
+            "kernels_us": {k: round(v["mean"], 2) for k, v in l["kern"].items()}}
     if not args.no_secondary:
-        sec = out.setdefault("secondary", {})
         sec["candidate_blocks"] = time_candidate_blocks(torch, device, args.steps)
         sec["grouped_output"] = {
             "decode64": time_grouped_output(torch, device, args.steps, 64),
             "prefill": time_grouped_output(torch, device, args.steps, 2048)}
     if not args.no_secondary and not args.rope:
         # the same step with the rotary epilogue in front (pre-rotation q and kv)
-        rw, rms, rk, rwork, rsep = run_workload(wl.name, args.steps, args.warmup,
-                                                args.input_sets, torch, device, rope=True,
-                                                separate=args.separate_calls)
-        out.setdefault("secondary", {})["with_rope_epilogue"] = {
-            "value": round(rw.queries / (rms * 1e-3), 1), "unit": "tokens/s",
-            "ms_per_step": round(rms, 5),
-            "ms_per_step_separate_calls": round(rsep, 5) if rsep is not None else None,
+        rr = run_workload(wl.name, args.steps, args.warmup, args.input_sets, torch, device,
+                          evict, rope=True, separate=args.separate_calls)
+        rw, rk, rwork = rr["wl"], rr["kern"], rr["work"]
+        sec["with_rope_epilogue"] = {
+            "value": round(rw.queries / (rr["ms_step"] * 1e-3), 1), "unit": "tokens/s",
+            "ms_per_step": round(rr["ms_step"], 5),
+            "ms_per_step_separate_calls": (round(rr["ms_sep"], 5) if rr["ms_sep"] is not None
+                                           else None),
             "rope_rows": roofline_entry("rope_rows", rwork, rk["rope_rows"], "hbm", rw.name),
             "rope_fp8_rows": roofline_entry("rope_fp8_rows", rwork, rk["rope_fp8_rows"], "hbm",
                                             rw.name),
-            "kernels_us": {k: round(v, 2) for k, v in rk.items()}}
-    if not args.no_cpu_baseline:
-        n = args.cpu_sample or (wl.batch if wl.mode == "decode" else 32)
-        t0 = time.time()
-        out["cpu_baseline"] = cpu_baseline(wl, n)
-        log(f"cpu baseline in {time.time() - t0:.1f}s")
+            "kernels_us": {k: round(v["mean"], 2) for k, v in rk.items()}}
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 

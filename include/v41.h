@@ -443,6 +443,26 @@ typedef struct v41_decode_step_args {
 
 int v41_decode_step(const v41_decode_step_args *args, v41_stream stream);
 
+/*
+ * Measurement helpers, not steps of the method: what this GPU reaches on
+ * plain work, for stating throughput against measured ceilings beside the
+ * published peaks.
+ *
+ * v41_probe_hbm_read reads `bytes` (a multiple of 16, buf 16-byte aligned)
+ * once, 16 bytes per lane, grid-stride over 2048 workgroups of 256 threads,
+ * with non-temporal loads when `nontemporal` is non-zero; nothing is
+ * written (`sink`, one uint32, is written only under a condition the data
+ * never meets, which keeps the loads).
+ * v41_probe_mfma runs `workgroups` workgroups of four wavefronts, each
+ * wavefront `iters` rounds of eight independent v_mfma_f32_16x16x32_bf16
+ * (16384 flops each) on register operands: 524288 * workgroups * iters flops;
+ * `sink` (one float) as above.
+ */
+int v41_probe_hbm_read(const void *buf, int64_t bytes, int32_t nontemporal,
+                       uint32_t *sink, v41_stream stream);
+int v41_probe_mfma(int32_t workgroups, int32_t iters, float *sink,
+                   v41_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -65,7 +65,7 @@ extern "C" {
 
 const char* v41_last_error(void) { return g_err; }
 
-int v41_abi_version(void) { return 6; }
+int v41_abi_version(void) { return 7; }
 
 int v41_fp8_round_rows(const v41_bf16* in, int64_t in_ld, v41_bf16* out, int64_t out_ld,
                        int64_t rows, int32_t row_len, v41_bf16* ring, int32_t ring_slots,
@@ -495,6 +495,29 @@ int v41_grouped_output(v41_bf16* o, int64_t n_tokens, int32_t n_heads,
   v41::LinearArgs l2{og, og_w, 0, wo_b, og_w, 0, x, dim, 0, M, dim, (int32_t)og_w, 1, workspace,
                      wb};
   return launched(v41::launch_linear_bf16(l2, s), "grouped_output wo_b");
+}
+
+int v41_probe_hbm_read(const void* buf, int64_t bytes, int32_t nontemporal, uint32_t* sink,
+                       v41_stream stream) {
+  if (bytes < 0 || bytes % 16 != 0)
+    return fail(V41_EINVAL, "probe_hbm_read: bytes must be a non-negative multiple of 16");
+  if (bytes > 0 && (buf == nullptr || sink == nullptr))
+    return fail(V41_EINVAL, "probe_hbm_read: NULL buf/sink");
+  if (!aligned16(buf)) return fail(V41_EINVAL, "probe_hbm_read: buf must be 16-byte aligned");
+  int rc = check_device();
+  if (rc) return rc;
+  if (bytes == 0) return V41_OK;
+  return launched(v41::launch_probe_hbm_read(buf, bytes, nontemporal, sink, (hipStream_t)stream),
+                  "probe_hbm_read");
+}
+
+int v41_probe_mfma(int32_t workgroups, int32_t iters, float* sink, v41_stream stream) {
+  if (workgroups < 1 || iters < 1 || sink == nullptr)
+    return fail(V41_EINVAL, "probe_mfma: workgroups and iters must be >= 1, sink non-NULL");
+  int rc = check_device();
+  if (rc) return rc;
+  return launched(v41::launch_probe_mfma(workgroups, iters, sink, (hipStream_t)stream),
+                  "probe_mfma");
 }
 
 int v41_decode_step(const v41_decode_step_args* a, v41_stream stream) {

@@ -79,6 +79,10 @@ struct AttnArgs {
   int64_t workspace_bytes;
 };
 
+hipError_t launch_probe_hbm_read(const void* buf, int64_t bytes, int32_t nontemporal,
+                                 uint32_t* sink, hipStream_t s);
+hipError_t launch_probe_mfma(int32_t workgroups, int32_t iters, float* sink, hipStream_t s);
+
 int attn_preferred_splits(int32_t queries, int32_t n_heads, int32_t width);
 int64_t attn_workspace_bytes(int32_t queries, int32_t n_heads, int32_t head_dim,
                              int32_t splits);

@@ -20,7 +20,7 @@ EXPORTS = ("v41_last_error", "v41_abi_version", "v41_fp8_round_rows", "v41_windo
            "v41_sparse_attn_workspace_bytes", "v41_rope_table", "v41_rope_rows",
            "v41_rope_fp8_rows", "v41_decode_step", "v41_candidate_blocks", "v41_linear_bf16",
            "v41_linear_workspace_bytes", "v41_grouped_output",
-           "v41_grouped_output_workspace_bytes")
+           "v41_grouped_output_workspace_bytes", "v41_probe_hbm_read", "v41_probe_mfma")
 
 
 class DecodeStepArgs(C.Structure):
@@ -108,6 +108,10 @@ def load() -> C.CDLL:
                                      i32, vp, i64, vp, i64, vp]
     L.v41_grouped_output_workspace_bytes.restype = C.c_int64
     L.v41_grouped_output_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i32]
+    L.v41_probe_hbm_read.restype = C.c_int
+    L.v41_probe_hbm_read.argtypes = [vp, i64, i32, vp, vp]
+    L.v41_probe_mfma.restype = C.c_int
+    L.v41_probe_mfma.argtypes = [i32, i32, vp, vp]
     L.v41_decode_step.restype = C.c_int
     L.v41_decode_step.argtypes = [C.POINTER(DecodeStepArgs), vp]
     _lib = L
@@ -242,3 +246,12 @@ def v41_grouped_output(o, n_tokens, n_heads, head_dim, groups, rank, dim, wo_a, 
 def v41_grouped_output_workspace_bytes(n_tokens, n_heads, head_dim, groups, rank, dim) -> int:
     return int(load().v41_grouped_output_workspace_bytes(n_tokens, n_heads, head_dim, groups,
                                                          rank, dim))
+
+
+def v41_probe_hbm_read(buf, nbytes, nontemporal, sink, stream=None) -> None:
+    _check(load().v41_probe_hbm_read(_ptr(buf), nbytes, int(nontemporal), _ptr(sink),
+                                     _stream(stream)))
+
+
+def v41_probe_mfma(workgroups, iters, sink, stream=None) -> None:
+    _check(load().v41_probe_mfma(workgroups, iters, _ptr(sink), _stream(stream)))

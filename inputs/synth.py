@@ -62,6 +62,16 @@ _PAR_BLOCK = 1 << 20
 _pool = None
 
 
+def _drop_pool_after_fork() -> None:
+    """A forked child inherits the pool object but not its threads: start a
+    new one there when needed."""
+    global _pool
+    _pool = None
+
+
+os.register_at_fork(after_in_child=_drop_pool_after_fork)
+
+
 def _w() -> _Work:
     w = getattr(_tls, "work", None)
     if w is None:
