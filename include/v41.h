@@ -9,7 +9,9 @@
  *  - bf16 values travel as raw uint16 bit patterns (v41_bf16).
  *  - Every data pointer is a device pointer owned by the caller; the library
  *    keeps no state between calls.  Only the calls with a `workspace`
- *    argument use scratch memory, and only the caller's.
+ *    argument use scratch memory, and only the caller's; the one exception
+ *    is v41_sparse_attn_sink_noalloc, which uses a static device array of
+ *    the library.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null
  *    stream) and never synchronise the host.
  *  - Strides ("_ld" between rows, "_bs" between sequences) count elements,
@@ -225,6 +227,38 @@ int v41_sparse_attn_sink(const v41_bf16 *q, const v41_bf16 *rows_a,
 int64_t v41_sparse_attn_workspace_bytes(int32_t batch, int32_t n_tokens,
                                         int32_t n_heads, int32_t head_dim,
                                         int32_t width);
+
+/* Bytes of the library's own device scratch array behind
+ * v41_sparse_attn_sink_noalloc (per GPU, held until the process ends). */
+#define V41_NOALLOC_SCRATCH_BYTES (32LL << 20)
+
+/*
+ * v41_sparse_attn_sink for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, meaning and result as v41_sparse_attn_sink
+ * with a workspace of v41_sparse_attn_workspace_bytes(...) bytes, except that
+ * the row-split partials go to a static device array of the library
+ * (V41_NOALLOC_SCRATCH_BYTES per GPU) instead of a caller's workspace.
+ *
+ *  - Calls no hipMalloc/hipFree and no allocating library routine.  The
+ *    first call on a device looks up that device's copy of the array
+ *    (hipGetSymbolAddress), with that device current.
+ *  - Returns V41_EINVAL, with a message, when the shape needs more than
+ *    V41_NOALLOC_SCRATCH_BYTES of scratch (v41_sparse_attn_workspace_bytes
+ *    tells how much it needs).
+ *  - Every call on one GPU shares that GPU's array, which keeps the last
+ *    call's partials: calls that overlap in time on one GPU (two streams,
+ *    two host threads) race and give undefined results.  Serialise them.
+ */
+int v41_sparse_attn_sink_noalloc(const v41_bf16 *q, const v41_bf16 *rows_a,
+                                 int64_t rows_a_len, int64_t a_bs,
+                                 const v41_bf16 *rows_b, int64_t rows_b_len,
+                                 int64_t b_bs, const int32_t *idx,
+                                 int32_t width, int64_t idx_ld,
+                                 const float *sink, float scale, int32_t batch,
+                                 int32_t n_tokens, int32_t n_heads,
+                                 int32_t head_dim, v41_bf16 *out,
+                                 v41_stream stream);
 
 /*
  * RoPE table at ratio 0 ("deepseek_v41_ref::attn": freqs_cis, the table

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/v41.h"
 #include "v41_common.h"
@@ -65,7 +66,7 @@ extern "C" {
 
 const char* v41_last_error(void) { return g_err; }
 
-int v41_abi_version(void) { return 7; }
+int v41_abi_version(void) { return 8; }
 
 int v41_fp8_round_rows(const v41_bf16* in, int64_t in_ld, v41_bf16* out, int64_t out_ld,
                        int64_t rows, int32_t row_len, v41_bf16* ring, int32_t ring_slots,
@@ -184,12 +185,45 @@ int64_t v41_sparse_attn_workspace_bytes(int32_t batch, int32_t n_tokens, int32_t
                                    v41::attn_preferred_splits(nq, n_heads, width));
 }
 
-int v41_sparse_attn_sink(const v41_bf16* q, const v41_bf16* rows_a, int64_t rows_a_len,
-                         int64_t a_bs, const v41_bf16* rows_b, int64_t rows_b_len, int64_t b_bs,
-                         const int32_t* idx, int32_t width, int64_t idx_ld, const float* sink,
-                         float scale, int32_t batch, int32_t n_tokens, int32_t n_heads,
-                         int32_t head_dim, v41_bf16* out, void* workspace,
-                         int64_t workspace_bytes, v41_stream stream) {
+}  // extern "C"
+
+namespace {
+
+// The device array behind v41_sparse_attn_sink_noalloc.  In host code its
+// name stands for a host-side shadow, not a device address: kernels get the
+// address hipGetSymbolAddress returns for the current device.
+__device__ __align__(256) uint8_t scratch[V41_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];  // per device ordinal, set on the first call there
+
+// This device's address of `scratch` (the device is current and checked).
+int scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(V41_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(V41_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return V41_OK;
+}
+
+// Checks and launch shared by the two attention entry points.  With
+// `noalloc`, the workspace arguments are ignored and the device scratch array
+// serves instead.
+int sparse_attn_call(const v41_bf16* q, const v41_bf16* rows_a, int64_t rows_a_len,
+                     int64_t a_bs, const v41_bf16* rows_b, int64_t rows_b_len, int64_t b_bs,
+                     const int32_t* idx, int32_t width, int64_t idx_ld, const float* sink,
+                     float scale, int32_t batch, int32_t n_tokens, int32_t n_heads,
+                     int32_t head_dim, v41_bf16* out, void* workspace, int64_t workspace_bytes,
+                     bool noalloc, v41_stream stream) {
   if (batch < 0 || n_tokens < 0 || rows_a_len < 0 || rows_b_len < 0)
     return fail(V41_EINVAL, "sparse_attn_sink: negative size");
   if (n_heads < 1) return fail(V41_EINVAL, "sparse_attn_sink: n_heads < 1");
@@ -221,6 +255,26 @@ int v41_sparse_attn_sink(const v41_bf16* q, const v41_bf16* rows_a, int64_t rows
   if (workspace_bytes < 0) return fail(V41_EINVAL, "sparse_attn_sink: workspace_bytes < 0");
   int rc = check_device();
   if (rc) return rc;
+  if (noalloc) {
+    // exactly the split the workspace-taking call prefers for this shape
+    const int64_t need = (nq > 0 && width > 0)
+                             ? v41::attn_workspace_bytes(
+                                   (int32_t)nq, n_heads, head_dim,
+                                   v41::attn_preferred_splits((int32_t)nq, n_heads, width))
+                             : 0;
+    if (need > V41_NOALLOC_SCRATCH_BYTES)
+      return fail(V41_EINVAL,
+                  "sparse_attn_sink_noalloc: this shape needs %lld bytes of scratch, more "
+                  "than the static %lld; call v41_sparse_attn_sink with a workspace",
+                  (long long)need, (long long)V41_NOALLOC_SCRATCH_BYTES);
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (need > 0) {
+      rc = scratch_address(&workspace);
+      if (rc) return rc;
+      workspace_bytes = need;
+    }
+  }
   v41::AttnArgs a;
   a.q = q;
   a.rows_a = rows_a;
@@ -241,7 +295,34 @@ int v41_sparse_attn_sink(const v41_bf16* q, const v41_bf16* rows_a, int64_t rows
   a.out = out;
   a.workspace = workspace;
   a.workspace_bytes = workspace ? workspace_bytes : 0;
-  return launched(v41::launch_sparse_attn_sink(a, (hipStream_t)stream), "sparse_attn_sink");
+  return launched(v41::launch_sparse_attn_sink(a, (hipStream_t)stream),
+                  noalloc ? "sparse_attn_sink_noalloc" : "sparse_attn_sink");
+}
+
+}  // namespace
+
+extern "C" {
+
+int v41_sparse_attn_sink(const v41_bf16* q, const v41_bf16* rows_a, int64_t rows_a_len,
+                         int64_t a_bs, const v41_bf16* rows_b, int64_t rows_b_len, int64_t b_bs,
+                         const int32_t* idx, int32_t width, int64_t idx_ld, const float* sink,
+                         float scale, int32_t batch, int32_t n_tokens, int32_t n_heads,
+                         int32_t head_dim, v41_bf16* out, void* workspace,
+                         int64_t workspace_bytes, v41_stream stream) {
+  return sparse_attn_call(q, rows_a, rows_a_len, a_bs, rows_b, rows_b_len, b_bs, idx, width,
+                          idx_ld, sink, scale, batch, n_tokens, n_heads, head_dim, out,
+                          workspace, workspace_bytes, false, stream);
+}
+
+int v41_sparse_attn_sink_noalloc(const v41_bf16* q, const v41_bf16* rows_a, int64_t rows_a_len,
+                                 int64_t a_bs, const v41_bf16* rows_b, int64_t rows_b_len,
+                                 int64_t b_bs, const int32_t* idx, int32_t width,
+                                 int64_t idx_ld, const float* sink, float scale, int32_t batch,
+                                 int32_t n_tokens, int32_t n_heads, int32_t head_dim,
+                                 v41_bf16* out, v41_stream stream) {
+  return sparse_attn_call(q, rows_a, rows_a_len, a_bs, rows_b, rows_b_len, b_bs, idx, width,
+                          idx_ld, sink, scale, batch, n_tokens, n_heads, head_dim, out, nullptr,
+                          0, true, stream);
 }
 
 int v41_rope_table(double theta, int32_t rope_dim, int64_t n_pos, float* table,

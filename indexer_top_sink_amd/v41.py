@@ -17,9 +17,9 @@ LIB_PATH = os.path.join(_HERE, "libv41.so")
 V41_OK, V41_EINVAL, V41_EHIP, V41_EDEVICE = 0, -1, -2, -3
 EXPORTS = ("v41_last_error", "v41_abi_version", "v41_fp8_round_rows", "v41_window_idx",
            "v41_indexer_scores", "v41_topk_select", "v41_sparse_attn_sink",
-           "v41_sparse_attn_workspace_bytes", "v41_rope_table", "v41_rope_rows",
-           "v41_rope_fp8_rows", "v41_decode_step", "v41_candidate_blocks", "v41_linear_bf16",
-           "v41_linear_workspace_bytes", "v41_grouped_output",
+           "v41_sparse_attn_workspace_bytes", "v41_sparse_attn_sink_noalloc", "v41_rope_table",
+           "v41_rope_rows", "v41_rope_fp8_rows", "v41_decode_step", "v41_candidate_blocks",
+           "v41_linear_bf16", "v41_linear_workspace_bytes", "v41_grouped_output",
            "v41_grouped_output_workspace_bytes", "v41_probe_hbm_read", "v41_probe_mfma")
 
 
@@ -86,6 +86,9 @@ def load() -> C.CDLL:
     L.v41_sparse_attn_sink.restype = C.c_int
     L.v41_sparse_attn_sink.argtypes = [vp, vp, i64, i64, vp, i64, i64, vp, i32, i64, vp, f32,
                                        i32, i32, i32, i32, vp, vp, i64, vp]
+    L.v41_sparse_attn_sink_noalloc.restype = C.c_int
+    L.v41_sparse_attn_sink_noalloc.argtypes = [vp, vp, i64, i64, vp, i64, i64, vp, i32, i64, vp,
+                                               f32, i32, i32, i32, i32, vp, vp]
     L.v41_sparse_attn_workspace_bytes.restype = C.c_int64
     L.v41_sparse_attn_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     L.v41_rope_table.restype = C.c_int
@@ -186,6 +189,16 @@ def v41_sparse_attn_sink(q, rows_a, rows_a_len, a_bs, rows_b, rows_b_len, b_bs, 
                                        float(scale), batch, n_tokens, n_heads, head_dim,
                                        _ptr(out), _ptr(workspace), workspace_bytes,
                                        _stream(stream)))
+
+
+def v41_sparse_attn_sink_noalloc(q, rows_a, rows_a_len, a_bs, rows_b, rows_b_len, b_bs, idx,
+                                 width, idx_ld, sink, scale, batch, n_tokens, n_heads, head_dim,
+                                 out, stream=None) -> None:
+    _check(load().v41_sparse_attn_sink_noalloc(_ptr(q), _ptr(rows_a), rows_a_len, a_bs,
+                                               _ptr(rows_b), rows_b_len, b_bs, _ptr(idx), width,
+                                               idx_ld, _ptr(sink), float(scale), batch,
+                                               n_tokens, n_heads, head_dim, _ptr(out),
+                                               _stream(stream)))
 
 
 def v41_sparse_attn_workspace_bytes(batch, n_tokens, n_heads, head_dim, width) -> int:

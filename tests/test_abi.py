@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version(lib):
-    assert lib.v41_abi_version() == 7
+    assert lib.v41_abi_version() == 8
 
 
 def _err(lib):
