@@ -41,11 +41,19 @@ def attn_report(gpu_bits: np.ndarray, ora_bits: np.ndarray) -> dict:
     }
 
 
-def assert_attn_close(gpu_bits, ora_bits, what=""):
+# Regression floor on the share of outputs within 2 bf16 ulp: with the
+# probabilities entering PV as a bf16 pair every case measured 99.97-100%
+# (the rest are outputs near zero, where the f32 accumulation error spans
+# many ulps of the output).
+MIN_WITHIN_2ULP = 0.999
+
+
+def assert_attn_close(gpu_bits, ora_bits, what="", min_within_2ulp=MIN_WITHIN_2ULP):
     r = attn_report(gpu_bits, ora_bits)
     print(f"[attn parity] {what} {r}", flush=True)
     assert r["finite"], what
     assert r["fail"] == 0, (what, r)
+    assert r["frac_within_2ulp"] >= min_within_2ulp, (what, r)
     return r
 
 
