@@ -20,10 +20,13 @@
 //
 // The epilogue applies ReLU and the weights in f32, sums the 4 heads a lane
 // holds per tile, then across the 4 lane groups with two xor-shuffles.  Keys
-// past the causal bound are never loaded and score -inf; with a candidate mask
-// each block's mask byte is requested just before the next stage's loads (so
-// its wait leaves them in flight) and the epilogue writes -inf for a masked
-// position (its products were computed and are discarded).
+// past the causal bound are never loaded and score -inf.  With a candidate
+// mask, a wavefront first finds which of its blocks hold an unmasked visible
+// position (64 blocks at a time, one lane per block reading the block's mask
+// bytes into a 16-bit keep mask, the live ones listed by a ballot): the
+// others score -inf without a key load or a matrix product, and the stream
+// runs over the live blocks with their keep masks in a register (no memory
+// access of the mask inside the stream, so no wait on it there).
 #include "v41_common.h"
 #include "v41_front.h"
 
@@ -129,6 +132,8 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(
   constexpr int kRingBytes = kStages * KT::kBytes;
   constexpr int kAux = NT ? 2 : 0;  // nt: no reuse expected
   __shared__ __attribute__((aligned(16))) uint8_t smem[kQBytes + 64 * 4 + kWaves * kRingBytes];
+  __shared__ int32_t wlist[kWaves][kWave];   // live block lists
+  __shared__ uint32_t wkeep[kWaves][kWave];  // and their 16-bit keep masks
   uint8_t* const qs = smem;
   float* const ws = reinterpret_cast<float*>(smem + kQBytes);
 
@@ -169,10 +174,57 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(
   uint8_t* const ring = smem + kQBytes + 64 * 4 + wave * kRingBytes;
   const uint16_t* __restrict__ kb = kI + b * kI_bs;
 
-  // ---- first kStages blocks in flight, then the query through LDS
+  // ---- this wavefront's blocks part + i wpq, i < nw, taken 64 at a time:
+  // with a mask, the live ones of a chunk are listed (lane l holds the
+  // l-th), the masked ones score -inf here
+  auto chunk_list = [&](int c0, int& n_live, uint32_t& keep) -> int32_t {
+    const int cn = nw - c0 < kWave ? nw - c0 : kWave;
+    keep = 0xFFFFu;  // without a mask: every position (the causal bound is checked apart)
+    if (cand == nullptr) {
+      n_live = cn;
+      return c0 + lane;
+    }
+    uint32_t km = 0u;  // bit p: position j0 + p is visible and unmasked
+    if (lane < cn) {
+      const int j0 = (part + (c0 + lane) * wpq) * 16;
+      const int j1 = j0 + 16 < live_end ? j0 + 16 : live_end;
+      for (int cb = j0 / cand_block; cb <= (j1 - 1) / cand_block; ++cb) {
+        if (cand[q * cand_width + cb] != 0) {
+          const int a = cb * cand_block > j0 ? cb * cand_block : j0;
+          const int e = (cb + 1) * cand_block < j1 ? (cb + 1) * cand_block : j1;
+          km |= ((1u << (e - a)) - 1u) << (a - j0);
+        }
+      }
+    }
+    const bool live = km != 0u;
+    const unsigned long long lm = __ballot(live);
+    n_live = __popcll(lm);
+    // masked blocks: -inf for their 16 positions
+    for (unsigned long long dm = __ballot(lane < cn && !live); dm != 0ull; dm &= dm - 1ull) {
+      const int j = (part + (c0 + __builtin_ctzll(dm)) * wpq) * 16 + lane;
+      if (lane < 16 && j < n_rows) srow[j] = -__builtin_huge_valf();
+    }
+    // lane l: the index and keep mask of the l-th live block (through
+    // per-wavefront lists)
+    if (live) {
+      const int rank = __popcll(lm & ((1ull << lane) - 1ull));
+      wlist[wave][rank] = c0 + lane;
+      wkeep[wave][rank] = km;
+    }
+    __builtin_amdgcn_wave_barrier();
+    keep = lane < n_live ? wkeep[wave][lane] : 0u;
+    return lane < n_live ? wlist[wave][lane] : 0;
+  };
+  int n_live0 = 0;
+  uint32_t keep0 = 0u;
+  const int32_t list0 = nw > 0 ? chunk_list(0, n_live0, keep0) : 0;
+
+  // ---- first kStages live blocks in flight, then the query through LDS
 #pragma unroll
   for (int s = 0; s < kStages; ++s)
-    if (s < nw) issue_block<DI, kAux>(kb, (part + s * wpq) * 16, live_end, lane, ring + s * KT::kBytes);
+    if (s < n_live0)
+      issue_block<DI, kAux>(kb, (part + __builtin_amdgcn_readlane(list0, s) * wpq) * 16,
+                            live_end, lane, ring + s * KT::kBytes);
   {
     const uint16_t* qrow = qI + q * n_heads * DI;
     for (int e = threadIdx.x; e < 16 * HT * KT::CPR; e += kThreads) {
@@ -215,55 +267,64 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(
     if (lane < 16 && j < n_rows) srow[j] = kNegInf;
   }
 
-  // ---- the stream
-  for (int i0 = 0; i0 < nw; i0 += kStages) {
+  // ---- the stream, over the live blocks of each chunk
+  int32_t list = list0;
+  uint32_t keepv = keep0;
+  int n_live = n_live0;
+  for (int c0 = 0; c0 < nw; c0 += kWave) {
+    if (c0 > 0) {
+      list = chunk_list(c0, n_live, keepv);
 #pragma unroll
-    for (int s = 0; s < kStages; ++s) {
-      const int i = i0 + s;
-      if (i < nw) {
-        if (i + kStages - 1 < nw) wait_vmcnt<KS * (kStages - 1)>();
-        else wait_vmcnt<0>();
-        u32x4 kf[KS];
-        lds_read_ks<KS>(kf, off, ring_lds + s * KT::kBytes);
-        // the block's mask byte, requested before the next stage's loads so
-        // that waiting for it leaves those in flight
-        const int jm = (part + i * wpq) * 16 + r16;
-        uint32_t keep = 1u;
-        if (cand != nullptr && g == 0 && jm < live_end)
-          keep = cand[q * cand_width + (uint32_t)jm / (uint32_t)cand_block];
-        if (i + kStages < nw)
-          issue_block<DI, kAux>(kb, (part + (i + kStages) * wpq) * 16, live_end, lane,
-                                ring + s * KT::kBytes);
-        f32x4 acc[HT];
+      for (int s = 0; s < kStages; ++s)
+        if (s < n_live)
+          issue_block<DI, kAux>(kb, (part + __builtin_amdgcn_readlane(list, s) * wpq) * 16,
+                                live_end, lane, ring + s * KT::kBytes);
+    }
+    for (int i0 = 0; i0 < n_live; i0 += kStages) {
 #pragma unroll
-        for (int ht = 0; ht < HT; ++ht) acc[ht] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < kStages; ++s) {
+        const int i = i0 + s;
+        if (i < n_live) {
+          if (i + kStages - 1 < n_live) wait_vmcnt<KS * (kStages - 1)>();
+          else wait_vmcnt<0>();
+          u32x4 kf[KS];
+          lds_read_ks<KS>(kf, off, ring_lds + s * KT::kBytes);
+          const int blk = part + __builtin_amdgcn_readlane(list, i) * wpq;
+          const uint32_t keep = (__builtin_amdgcn_readlane(keepv, i) >> r16) & 1u;
+          if (i + kStages < n_live)
+            issue_block<DI, kAux>(
+                kb, (part + __builtin_amdgcn_readlane(list, i + kStages) * wpq) * 16, live_end,
+                lane, ring + s * KT::kBytes);
+          f32x4 acc[HT];
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          const bf16x8 bk = as_bf16x8(kf[kk]);
+          for (int ht = 0; ht < HT; ++ht) acc[ht] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma16x16x32(afr[ht][kk], bk, acc[ht]);
+          for (int kk = 0; kk < KS; ++kk) {
+            const bf16x8 bk = as_bf16x8(kf[kk]);
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) acc[ht] = mfma16x16x32(afr[ht][kk], bk, acc[ht]);
+          }
+          float sum = 0.0f;
+#pragma unroll
+          for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sum += wh[ht][e] * fmaxf(acc[ht][e], 0.0f);
+          {
+            // the four k-groups' partial sums of the key (lanes 16 and 32
+            // apart), on the permlane swaps
+            const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(sum),
+                                                            __float_as_uint(sum), false, false);
+            sum = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+            const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum),
+                                                            __float_as_uint(sum), false, false);
+            sum = __uint_as_float(t[0]) + __uint_as_float(t[1]);
+          }
+          const int j = blk * 16 + r16;
+          if (g == 0 && j < n_rows) srow[j] = (j < live_end && keep != 0u) ? sum : kNegInf;
         }
-        float sum = 0.0f;
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sum += wh[ht][e] * fmaxf(acc[ht][e], 0.0f);
-        {
-          // the four k-groups' partial sums of the key (lanes 16 and 32
-          // apart), on the permlane swaps
-          const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(sum),
-                                                          __float_as_uint(sum), false, false);
-          sum = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-          const auto t = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum),
-                                                          __float_as_uint(sum), false, false);
-          sum = __uint_as_float(t[0]) + __uint_as_float(t[1]);
-        }
-        const int j = (part + i * wpq) * 16 + r16;
-        if (g == 0 && j < n_rows) srow[j] = (j < live_end && keep != 0u) ? sum : kNegInf;
       }
     }
   }
-
 }
 
 template <int DI, int NT>

@@ -172,6 +172,41 @@ def test_indexer_candidate_mask(v41):
     assert_scores_close(got, ora, "masked")
 
 
+@pytest.mark.parametrize("blk", [1, 5, 8, 16, 24, 64])
+def test_indexer_mask_blocks(v41, blk):
+    """Mask blocks shorter than, equal to, longer than and not aligned with
+    the kernel's 16-key blocks: a key block is skipped only when none of its
+    visible positions is unmasked, and a partly masked one scores -inf at
+    its masked positions."""
+    T, HI, DI, L = 300, 64, 128, 1000
+    say("indexer mask blocks", blk)
+    rng = np.random.default_rng(100 + blk)
+    qI = bf16_of(rng.standard_normal((T, HI, DI)))
+    kI = bf16_of(rng.standard_normal((1, L, DI)))
+    w = (rng.uniform(0, 1, (T, HI)) / 64).astype(np.float32)
+    nb = (L + blk - 1) // blk
+    cand = (rng.uniform(size=(T, nb)) < 0.4).astype(np.uint8)
+    got = run_indexer(v41, qI, kI, w, 0, 1, cand=cand, cand_block=blk)
+    ora = O.indexer_scores(qI, kI[0], w, 0, 1, cand=cand, cand_block=blk)
+    assert_scores_close(got, ora, f"mask blocks of {blk}")
+
+
+def test_indexer_mask_long_rows(v41):
+    """5000 tokens at ratio 1: the last tokens' wavefronts own more than 64
+    key blocks each, so their live-block lists are built 64 blocks at a time."""
+    T, HI, DI, L, blk = 5000, 4, 32, 5000, 16
+    say("indexer mask long rows", T)
+    rng = np.random.default_rng(5)
+    qI = bf16_of(rng.standard_normal((T, HI, DI)))
+    kI = bf16_of(rng.standard_normal((1, L, DI)))
+    w = rng.uniform(0, 1, (T, HI)).astype(np.float32)
+    cand = (rng.uniform(size=(T, (L + blk - 1) // blk)) < 0.5).astype(np.uint8)
+    toks = [0, 1, 17, 1023, 1024, 2999, 4095, 4998, 4999]
+    got = run_indexer(v41, qI, kI, w, 0, 1, cand=cand, cand_block=blk)[toks]
+    ora = O.indexer_scores(qI, kI[0], w, 0, 1, cand=cand, cand_block=blk, tokens=toks)
+    assert_scores_close(got, ora, "long masked rows")
+
+
 def test_indexer_zero_keys_give_zero(v41):
     HI, DI, L = 64, 128, 96
     rng = np.random.default_rng(8)
@@ -253,6 +288,45 @@ def test_topk_big_tie_group_straddles_k(v41):
     s = rng.uniform(0, 1, (2, L)).astype(np.float32)
     pos = rng.permutation(L)[:301]
     s[:, pos] = np.sort(s[0])[-400]
+    got = run_topk(v41, s, k, 128)
+    assert np.array_equal(got, O.topk(s, k, 128))
+
+
+@pytest.mark.parametrize("L", [8192, 32768])
+@pytest.mark.parametrize("layout", ["fallback", "single_key_bins", "whole_bin", "in_bin_passes",
+                                    "zeros_tie"])
+def test_topk_binned_paths(v41, L, layout):
+    """Rows shaped to take each branch of the long-row select (a 10-bit
+    histogram of key - min, then the threshold bin): bin b holding more than
+    2048 distinct keys (the full radix select), a key range under 1024 (each
+    bin one key value), the selection ending exactly at a bin's bottom, a
+    threshold bin of 1500 distinct keys whose select takes three 8-bit
+    passes, and a bin of 32k equal zeros (one value)."""
+    say("topk binned", L, layout)
+    rng = np.random.default_rng(L + len(layout))
+    k = 512
+    if layout == "fallback":
+        s = np.full(L, -1e30, dtype=np.float32)
+        s[rng.integers(0, L)] = 1e30
+        pos = rng.permutation(L)[:3000]
+        s[pos] = 1.0 + np.arange(3000, dtype=np.float32) * np.float32(2.0 ** -20)
+    elif layout == "single_key_bins":
+        s = (1.0 + rng.integers(0, 1000, L) * 2.0 ** -23).astype(np.float32)
+    elif layout == "whole_bin":
+        s = rng.uniform(0, 1, L).astype(np.float32)
+        pos = rng.permutation(L)[:k]
+        s[pos] = (100.0 + rng.uniform(0, 1, k)).astype(np.float32)
+    elif layout == "in_bin_passes":
+        s = np.full(L, -1e30, dtype=np.float32)
+        s[rng.integers(0, L)] = 1e30
+        pos = rng.permutation(L)[:1500]
+        s[pos] = 1.0 + rng.permutation(1500).astype(np.float32) * np.float32(2.0 ** -20)
+    else:
+        s = np.zeros(L, dtype=np.float32)
+        s[rng.uniform(size=L) < 0.5] = -0.0
+        pos = rng.permutation(L)[:300]
+        s[pos] = rng.uniform(0.1, 1, 300).astype(np.float32)
+    s = s[None, :]
     got = run_topk(v41, s, k, 128)
     assert np.array_equal(got, O.topk(s, k, 128))
 
