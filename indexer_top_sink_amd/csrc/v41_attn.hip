@@ -525,9 +525,12 @@ __global__ __launch_bounds__(kThreads, NS == 2 ? 2 : 1) void attn_kernel(Params 
 //    used from registers) and come back transposed (ds_read_b64_tr_b16) as
 //    the A operand of O^T += G^T P^T, all D dims;
 //  * QK: 16 rows x 16 heads over four independent accumulators; the S
-//    accumulator is laid out as the B operand of a 16x16x16 PV product, so
-//    the probabilities (a bf16 high part and remainder, one product each)
-//    never leave the lane;
+//    accumulator is laid out as the B operand of a 16-row PV product, so
+//    the probabilities never leave the lane.  They enter as a bf16 pair
+//    (high part and remainder) stacked on K of one 16x16x32 product whose A
+//    operand holds the transposed rows twice: O^T += [G^T G^T] [P_hi; P_lo].
+//    On this chip a 16x16x16 product takes as long as a 16x16x32 one, so the
+//    pair costs no more than a single bf16 P;
 //  * head maxima and sums across the lane groups use permlane swaps;
 //  * no barrier inside the loop; at the end the eight (max, sum, O) are
 //    merged through LDS, half of the dims at a time.
@@ -535,11 +538,14 @@ constexpr int kWaveRows = 16;
 constexpr int kNarrowHeads = 16;
 constexpr int kNarrowThreads = 512;
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4 mfma16x16x16(u32x2 a, u32x2 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
-                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+// One 16x16x32 product sums a_lane[s] * b_lane'[s] over the four lane
+// groups and the eight slots s, pairing the operands' slots one to one
+// (whatever k each names).  With the four values of a repeated in slots 4-7
+// and b = {four high parts, four remainders}, c += a * (b_hi + b_lo) over
+// the 16 rows of a 16x16x16 product.
+__device__ __forceinline__ f32x4 mfma_pair(u32x2 a, u32x4 b, f32x4 c) {
+  const u32x4 aa = {a[0], a[1], a[0], a[1]};
+  return mfma16x16x32(as_bf16x8(aa), as_bf16x8(b), c);
 }
 
 // v combined (max or sum) over the four 16-lane groups of the wavefront.
@@ -783,24 +789,21 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_narrow_kernel(Params p
       pl[e / 2] = (uint32_t)__builtin_bit_cast(uint16_t, c0) |
                   ((uint32_t)__builtin_bit_cast(uint16_t, c1) << 16);
     }
-    // O^T[dims][head] += G^T[dims][16 rows] P^T[16 rows][head]
+    // O^T[dims][head] += G^T[dims][16 rows] (P_hi + P_lo)^T[16 rows][head]
+    const u32x4 pp = {pk[0], pk[1], pl[0], pl[1]};
     if constexpr (DT >= 8) {
 #pragma unroll
       for (int d0 = 0; d0 < DT; d0 += 8) {
         u32x2 t[8];
         tr_load8(t, tr_addr + 32 * d0);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc_o[d0 + j] = mfma16x16x16(t[j], pk, acc_o[d0 + j]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc_o[d0 + j] = mfma16x16x16(t[j], pl, acc_o[d0 + j]);
+        for (int j = 0; j < 8; ++j) acc_o[d0 + j] = mfma_pair(t[j], pp, acc_o[d0 + j]);
       }
     } else {
       u32x2 t[4];
       tr_load4_1(t, tr_addr);
 #pragma unroll
-      for (int j = 0; j < DT; ++j) acc_o[j] = mfma16x16x16(t[j], pk, acc_o[j]);
-#pragma unroll
-      for (int j = 0; j < DT; ++j) acc_o[j] = mfma16x16x16(t[j], pl, acc_o[j]);
+      for (int j = 0; j < DT; ++j) acc_o[j] = mfma_pair(t[j], pp, acc_o[j]);
     }
     cur = nxt;
     vm_cur = vm_nxt;
