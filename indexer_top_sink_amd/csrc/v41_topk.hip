@@ -527,22 +527,29 @@ __global__ __launch_bounds__(kWave * kWaveRowsPerBlock) void topk_wave_kernel(
 }
 
 // Long rows: each thread owns a contiguous range and re-reads its scores.
-template <int NT>
-__global__ __launch_bounds__(NT) void topk_mem_kernel(const float* __restrict__ scores,
-                                                      int32_t n_cols, int64_t scores_ld,
-                                                      int32_t k, int32_t offset,
-                                                      int32_t* __restrict__ idx,
-                                                      int64_t idx_ld) {
-  __shared__ TopkShared<NT> sh;
+template <int NT, int HC>
+__device__ __forceinline__ void mem_select(const float* __restrict__ srow, int32_t n_cols,
+                                           int32_t k, int32_t offset,
+                                           int32_t* __restrict__ orow, TopkShared<NT, HC>& sh) {
   const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
-  const float* __restrict__ srow = scores + row * scores_ld;
-  int32_t* __restrict__ orow = idx + row * idx_ld;
   const int32_t C = (n_cols + NT - 1) / NT;
   const int32_t lo = tid * C;
   const int32_t hi = lo + C < n_cols ? lo + C : n_cols;
+  // the counting passes read the row strided (coalesced; their order does
+  // not matter) with eight loads in flight per thread, the output pass in
+  // contiguous ranges
+  constexpr int U = 8;
   auto for_keys = [&](auto f) {
-    for (int32_t j = lo; j < hi; ++j) f(score_key(srow[j]));
+    for (int32_t j0 = tid; j0 < n_cols; j0 += NT * U) {
+      float v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int32_t j = j0 + u * NT;
+        v[u] = j < n_cols ? srow[j] : -__builtin_huge_valf();
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) f(score_key(v[u]));
+    }
   };
 
   uint32_t nv_t = 0, kmin_t = 0xFFFFFFFFu, kmax_t = 0u;
@@ -560,25 +567,49 @@ __global__ __launch_bounds__(NT) void topk_mem_kernel(const float* __restrict__ 
   if (nv > (uint32_t)k) radix_select<NT>(for_keys, m, kmin, kmax, sh, T, need);
 
   uint32_t cg = 0, ce = 0;
-  for_keys([&](uint32_t key) {
-    cg += key > T;
-    ce += (need != 0u) && (key == T);
-  });
+  for (int32_t j0 = lo; j0 < hi; j0 += U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = j0 + u < hi ? srow[j0 + u] : -__builtin_huge_valf();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t key = score_key(v[u]);
+      cg += key > T;
+      ce += (need != 0u) && (key == T);
+    }
+  }
   // counts can exceed 16 bits here: two scans
   const uint32_t base_g = block_excl_scan<NT>(cg, sh);
   const uint32_t base_e = block_excl_scan<NT>(ce, sh);
   uint32_t pos = base_g + (base_e < need ? base_e : need);
   uint32_t er = base_e;
-  for (int32_t j = lo; j < hi; ++j) {
-    const uint32_t key = score_key(srow[j]);
-    if (key > T) {
-      orow[pos++] = j + offset;
-    } else if (need != 0u && key == T) {
-      if (er < need) orow[pos++] = j + offset;
-      ++er;
+  for (int32_t j0 = lo; j0 < hi; j0 += U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = j0 + u < hi ? srow[j0 + u] : -__builtin_huge_valf();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t key = score_key(v[u]);
+      if (key > T) {
+        orow[pos++] = j0 + u + offset;
+      } else if (need != 0u && key == T) {
+        if (er < need) orow[pos++] = j0 + u + offset;
+        ++er;
+      }
     }
   }
   for (int32_t i = (int32_t)m + tid; i < k; i += NT) orow[i] = -1;
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_mem_kernel(const float* __restrict__ scores,
+                                                      int32_t n_cols, int64_t scores_ld,
+                                                      int32_t k, int32_t offset,
+                                                      int32_t* __restrict__ idx,
+                                                      int64_t idx_ld) {
+  __shared__ TopkShared<NT> sh;
+  const int64_t row = blockIdx.x;
+  mem_select<NT>(scores + row * scores_ld, n_cols, k, offset, idx + row * idx_ld, sh);
 }
 
 // Candidate blocks of a score row: block b covers positions [b*cb, (b+1)*cb);

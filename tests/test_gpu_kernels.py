@@ -292,17 +292,16 @@ def test_topk_big_tie_group_straddles_k(v41):
     assert np.array_equal(got, O.topk(s, k, 128))
 
 
-@pytest.mark.parametrize("L", [8192, 32768])
+@pytest.mark.parametrize("L", [8192, 32768, 40000])
 @pytest.mark.parametrize("layout", ["fallback", "single_key_bins", "whole_bin", "in_bin_passes",
                                     "zeros_tie"])
-def test_topk_binned_paths(v41, L, layout):
-    """Rows shaped to take each branch of the long-row select (a 10-bit
-    histogram of key - min, then the threshold bin): bin b holding more than
-    2048 distinct keys (the full radix select), a key range under 1024 (each
-    bin one key value), the selection ending exactly at a bin's bottom, a
-    threshold bin of 1500 distinct keys whose select takes three 8-bit
-    passes, and a bin of 32k equal zeros (one value)."""
-    say("topk binned", L, layout)
+def test_topk_radix_layouts(v41, L, layout):
+    """Rows shaped to stress the radix passes: 3000 keys packed 2^-20 apart
+    between two extremes, a key range under 1024 values, a selection that
+    ends exactly at the bottom of a digit bin, a threshold group of 1500 close
+    keys that takes three 8-bit passes, and 32k equal zeros.  Rows of 40000
+    scores take the select that re-reads the row from memory."""
+    say("topk radix layouts", L, layout)
     rng = np.random.default_rng(L + len(layout))
     k = 512
     if layout == "fallback":
