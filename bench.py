@@ -24,7 +24,8 @@ launches the kernel once on each input set, directly, between two events, so
 every launch reads its data from HBM; mean, p50 and p90 over the reps of the
 per-launch time.  Rooflines use the mean.
 Fractions are given against the published peaks and against ceilings measured
-in the same run (a 1 GiB device copy; an 8192^3 bf16 torch.mm).
+in the same run (the library's HBM read and matrix-core probes; a 2 GiB device
+copy and an 8192^3 bf16 torch.mm are reported beside them).
 
 The CPU baseline is the oracle (plain C), run before the GPU is touched: one
 thread on a bounded sample, and a process pool over the step's sequences
