@@ -30,7 +30,7 @@ copy and an 8192^3 bf16 torch.mm are reported beside them).
 The CPU baseline is the oracle (plain C), run before the GPU is touched: one
 thread on a bounded sample, and a process pool over the step's sequences
 (tokens) on the host cores available (at most 16), with the core count and
-CPU model.
+CPU model; the prefill and decode16 lines carry the same two legs.
 
 With --rope the step starts from q and kv rows before their rotation: q is
 rotated in place and the fp8 call becomes the fused rotation + fp8 + ring write
@@ -770,6 +770,16 @@ def main():
         cpu = cpu_baseline(wl)
         log(f"cpu baseline in {time.time() - t0:.1f}s: {cpu['value']:.2f} tokens/s on "
             f"{cpu['cores']} processes, {cpu['single_thread']['value']:.2f} on one thread")
+    # the same two legs for the secondary workloads, on a smaller budget
+    cpu_sec = {}
+    if cpu is not None and not args.no_secondary:
+        for name in ("prefill", "decode16"):
+            if name == wl.name:
+                continue
+            t0 = time.time()
+            cpu_sec[name] = cpu_baseline(WL.WORKLOADS[name], budget_s=5.0)
+            log(f"cpu baseline {name} in {time.time() - t0:.1f}s: "
+                f"{cpu_sec[name]['value']:.2f} tokens/s on {cpu_sec[name]['cores']} processes")
 
     import torch
     device = torch.device("cuda:0")
@@ -851,11 +861,15 @@ def main():
             "indexer_roofline": roofline_entry("indexer_scores", pwork, pk["indexer_scores"],
                                                "mfma", pw.name, ceilings),
             "kernels_us": {k: round(v["mean"], 2) for k, v in pk.items()}}
+        if "prefill" in cpu_sec:
+            sec["prefill"]["cpu_baseline"] = cpu_sec["prefill"]
     if not args.no_secondary and wl.name != "decode16":
         # 16 sequences at context 131072 with the planted ties
         d = run_workload("decode16", args.steps, args.warmup, args.input_sets, torch, device,
                          evict, separate=args.separate_calls)
         sec["decode16"] = decode_summary(d, ceilings)
+        if "decode16" in cpu_sec:
+            sec["decode16"]["cpu_baseline"] = cpu_sec["decode16"]
     if not args.no_secondary and wl.name != "decode1":
         # one sequence at context 4096: the step's latency floor (its 1 MB of
         # data stays in the last-level cache between steps)
