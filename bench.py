@@ -453,35 +453,42 @@ def time_grouped_output(torch, device, steps, n_tokens):
 # ----------------------------------------------------------------- CPU baseline
 def _oracle_decode(job):
     """Worker: the oracle's decode step for each listed sequence; returns
-    (sequences done, seconds inside the oracle)."""
+    (sequences done, seconds inside the oracle, {sequence: (idx, out)} when
+    asked to keep the outputs)."""
     import oracle as O
     from oracle import layer as OL
-    name, seqs = job
+    name, seqs, keep = job
     wl = WL.WORKLOADS[name]
     sink = WL.layer_sink(wl)
     busy = 0.0
+    outs = {}
     for b in seqs:
         d = WL.decode_sequence(wl, b)
         ring = O.WindowCache(wl.window, wl.head_dim)
         ring.rows[:] = O.fp8_round_rows(d["ring_raw"])
         t0 = time.perf_counter()
-        OL.decode(ring, d["kv_new"], wl.start_pos, d["q"], sink, wl.scale, ratio=wl.ratio,
-                  latent=d["latent"], kI=d["kI"], qI=d["qI"], w=d["w"], k=wl.topk)
+        res = OL.decode(ring, d["kv_new"], wl.start_pos, d["q"], sink, wl.scale, ratio=wl.ratio,
+                        latent=d["latent"], kI=d["kI"], qI=d["qI"], w=d["w"], k=wl.topk)
         busy += time.perf_counter() - t0
-    return len(seqs), busy
+        if keep:
+            outs[b] = (res["idx"][0], res["out"][0])
+    return len(seqs), busy, outs
 
 
 def _oracle_prefill(job):
-    """Worker: the oracle's prefill chunk over the listed tokens."""
+    """Worker: the oracle's prefill chunk over the listed tokens (and, when
+    asked, their idx rows and outputs)."""
     from oracle import layer as OL
-    name, toks = job
+    name, toks, keep = job
     wl = WL.WORKLOADS[name]
     d = WL.prefill_inputs(wl)
     t0 = time.perf_counter()
-    OL.prefill(d["kv_chunk"], d["q"], WL.layer_sink(wl), wl.scale, wl.window, ratio=wl.ratio,
-               latent=d["latent"], kI=d["kI"], qI=d["qI"], w=d["w"], cand=d["cand"],
-               cand_block=wl.cand_block, k=wl.topk, queries=list(toks))
-    return len(toks), time.perf_counter() - t0
+    res = OL.prefill(d["kv_chunk"], d["q"], WL.layer_sink(wl), wl.scale, wl.window,
+                     ratio=wl.ratio, latent=d["latent"], kI=d["kI"], qI=d["qI"], w=d["w"],
+                     cand=d["cand"], cand_block=wl.cand_block, k=wl.topk, queries=list(toks))
+    t = time.perf_counter() - t0
+    outs = {t_: (res["idx"][i], res["out"][i]) for i, t_ in enumerate(toks)} if keep else {}
+    return len(toks), t, outs
 
 
 def host_cpu():
@@ -512,34 +519,37 @@ def cpu_baseline(wl, budget_s=10.0, max_workers=16):
     import multiprocessing as mp
     model, nproc, avail = host_cpu()
     workers = max(1, min(max_workers, avail))
+    outputs = {}  # the single-thread leg's oracle results, for the parity report
     if wl.mode == "decode":
         done, busy = 0, 0.0
         while done < wl.batch and busy < budget_s:
-            n, t = _oracle_decode((wl.name, [done]))
+            n, t, o = _oracle_decode((wl.name, [done], True))
             done += n
             busy += t
+            outputs.update(o)
         single = {"value": done / busy, "seconds": round(busy, 3),
                   "sample": f"{done} of {wl.batch} sequences, one decode step each"}
         chunks = [list(range(wl.batch))[i::workers] for i in range(workers)]
-        jobs = [(wl.name, c) for c in chunks if c]
+        jobs = [(wl.name, c, False) for c in chunks if c]
         fn = _oracle_decode
         unit_name = "sequences"
     else:
         toks = list(range(wl.n_tokens - 16, wl.n_tokens))    # the costliest tokens
-        n, t = _oracle_prefill((wl.name, toks))
+        n, t, outputs = _oracle_prefill((wl.name, toks, True))
         single = {"value": n / t, "seconds": round(t, 3),
                   "sample": f"the last {n} of {wl.n_tokens} prefill tokens (the longest rows)"}
         span = list(range(wl.n_tokens - 16 * workers, wl.n_tokens))
-        jobs = [(wl.name, span[i::workers]) for i in range(workers)]
+        jobs = [(wl.name, span[i::workers], False) for i in range(workers)]
         fn = _oracle_prefill
         unit_name = "tokens"
     t0 = time.perf_counter()
     with mp.get_context("fork").Pool(len(jobs)) as pool:
         res = pool.map(fn, jobs)
     wall = time.perf_counter() - t0
-    n_all = sum(n for n, _ in res)
-    busiest = max(t for _, t in res)
+    n_all = sum(r[0] for r in res)
+    busiest = max(r[1] for r in res)
     return {"value": round(n_all / busiest, 3), "unit": "tokens/s", "cores": len(jobs),
+            "_outputs": outputs,
             "kind": "oracle",
             "sample": f"{n_all} {unit_name} of one step over {len(jobs)} worker processes "
                       f"(throughput = work / busiest worker's oracle seconds)",
@@ -548,6 +558,53 @@ def cpu_baseline(wl, budget_s=10.0, max_workers=16):
                                  for k, v in single.items()}, "unit": "tokens/s",
                               "cores": 1},
             "cpu_model": model, "nproc": nproc, "cores_available": avail}
+
+
+# ------------------------------------------------------------- parity
+ATTN_ULPS, ATTN_ATOL = 2.0, 1e-2   # the attention parity criterion of the tests
+
+
+def _bf16_f64(bits):
+    w = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return w.view(np.float32).astype(np.float64)
+
+
+def parity_report(buf, wl, oracle_outputs):
+    """GPU results of input set 0 against the oracle results that the CPU leg
+    kept (its single-thread sample): the selected rows (window part exactly,
+    the top-k part as a set) and, where both sides selected the same rows,
+    the attention output in bf16 ulp of the oracle's value (pass: within 2
+    ulp or 1e-2 absolute)."""
+    from indexer_top_sink_amd import layer as LY
+    if not oracle_outputs:
+        return None
+    keys = sorted(oracle_outputs)
+    idx = buf.idx.cpu().numpy()
+    out = LY.to_numpy_bf16(buf.out)
+    W = idx.shape[1] - wl.topk
+    same, errs_ulp, errs_abs = 0, [], []
+    for r in keys:
+        o_idx, o_out = oracle_outputs[r]
+        if not (np.array_equal(idx[r, :W], o_idx[:W]) and
+                np.array_equal(np.sort(idx[r, W:]), np.sort(o_idx[W:]))):
+            continue
+        same += 1
+        g, o = _bf16_f64(out[r]), _bf16_f64(o_out)
+        err = np.abs(g - o)
+        ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(o), 2.0 ** -126))) - 7)
+        errs_ulp.append((err / ulp).ravel())
+        errs_abs.append(err.ravel())
+    unit = "sequences" if wl.mode == "decode" else "tokens"
+    rep = {"sample": f"{len(keys)} {unit} ({unit[:-1]} {keys[0]}..{keys[-1]}), the CPU leg's "
+                     "oracle outputs against the GPU step on the same inputs",
+           "selection_equal": f"{same} of {len(keys)}"}
+    if errs_ulp:
+        u, a = np.concatenate(errs_ulp), np.concatenate(errs_abs)
+        rep.update({"outputs": int(u.size), "max_ulp": round(float(u.max()), 2),
+                    "frac_within_2ulp": round(float((u <= ATTN_ULPS).mean()), 6),
+                    "max_abs": float(a.max()),
+                    "fail": int(((u > ATTN_ULPS) & (a > ATTN_ATOL)).sum())})
+    return rep
 
 
 # ----------------------------------------------------------------- main
@@ -590,7 +647,7 @@ def fused_call(buf, rope):
 
 
 def run_workload(name, steps, warmup, n_sets, torch, device, evict, rope=False,
-                 separate=False):
+                 separate=False, oracle_outputs=None):
     """Times K steps of a workload.  A decode step is one v41_decode_step call
     (unless separate); its separate-call form is timed alongside.  Per-kernel
     times: each kernel launched once on each input set in one graph, every
@@ -632,6 +689,7 @@ def run_workload(name, steps, warmup, n_sets, torch, device, evict, rope=False,
     graphs[0].replay()
     torch.cuda.synchronize()
 
+    parity = parity_report(sets[0], wl, oracle_outputs) if not rope else None
     idx = sets[0].idx.cpu().numpy()
     pairs = None
     if wl.mode == "prefill":
@@ -645,7 +703,7 @@ def run_workload(name, steps, warmup, n_sets, torch, device, evict, rope=False,
     del sets, calls, sep_fns, graphs
     torch.cuda.empty_cache()
     return {"wl": wl, "ms_step": ms_step, "step_stats": st_stats, "kern": kern, "work": work,
-            "ms_sep": ms_sep, "sep_stats": sep_stats}
+            "ms_sep": ms_sep, "sep_stats": sep_stats, "parity": parity}
 
 
 # Sources of each kernel: a stored traffic figure holds only while they are
@@ -765,9 +823,11 @@ def main():
 
     # the oracle first, before anything touches the GPU (its pool forks)
     cpu = None
+    oracle_out = {}
     if not args.no_cpu_baseline and not args.output_side:
         t0 = time.time()
         cpu = cpu_baseline(wl)
+        oracle_out[wl.name] = cpu.pop("_outputs")
         log(f"cpu baseline in {time.time() - t0:.1f}s: {cpu['value']:.2f} tokens/s on "
             f"{cpu['cores']} processes, {cpu['single_thread']['value']:.2f} on one thread")
     # the same two legs for the secondary workloads, on a smaller budget
@@ -778,6 +838,7 @@ def main():
                 continue
             t0 = time.time()
             cpu_sec[name] = cpu_baseline(WL.WORKLOADS[name], budget_s=5.0)
+            oracle_out[name] = cpu_sec[name].pop("_outputs")
             log(f"cpu baseline {name} in {time.time() - t0:.1f}s: "
                 f"{cpu_sec[name]['value']:.2f} tokens/s on {cpu_sec[name]['cores']} processes")
 
@@ -808,7 +869,8 @@ def main():
     log(f"measured ceilings: {ceilings}")
     evict = CacheEvictor(torch, device)
     r = run_workload(args.workload, args.steps, args.warmup, args.input_sets, torch, device,
-                     evict, rope=args.rope, separate=args.separate_calls)
+                     evict, rope=args.rope, separate=args.separate_calls,
+                     oracle_outputs=oracle_out.get(wl.name))
     kern, work, ms_step = r["kern"], r["work"], r["ms_step"]
     tokens = wl.queries
     value = tokens / (ms_step * 1e-3)
@@ -845,13 +907,14 @@ def main():
         "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "ms_per_step_separate_calls": round(r["ms_sep"], 5) if r["ms_sep"] is not None else None,
         "kernels_us": {k: round(v["mean"], 2) for k, v in kern.items()},
+        "parity": r["parity"],
     }
     if wl.mode == "decode":
         out["path_hbm_frac"] = path_frac(r)
     sec = out.setdefault("secondary", {}) if not args.no_secondary else {}
     if not args.no_secondary and wl.name != "prefill":
         p = run_workload("prefill", max(12, args.steps // 2), 3, args.input_sets, torch, device,
-                         evict)
+                         evict, oracle_outputs=oracle_out.get("prefill"))
         pw, pk, pwork = p["wl"], p["kern"], p["work"]
         sec["prefill"] = {
             "value": round(pw.n_tokens / (p["ms_step"] * 1e-3), 1), "unit": "tokens/s",
@@ -860,14 +923,17 @@ def main():
                                        "mfma", pw.name, ceilings),
             "indexer_roofline": roofline_entry("indexer_scores", pwork, pk["indexer_scores"],
                                                "mfma", pw.name, ceilings),
-            "kernels_us": {k: round(v["mean"], 2) for k, v in pk.items()}}
+            "kernels_us": {k: round(v["mean"], 2) for k, v in pk.items()},
+            "parity": p["parity"]}
         if "prefill" in cpu_sec:
             sec["prefill"]["cpu_baseline"] = cpu_sec["prefill"]
     if not args.no_secondary and wl.name != "decode16":
         # 16 sequences at context 131072 with the planted ties
         d = run_workload("decode16", args.steps, args.warmup, args.input_sets, torch, device,
-                         evict, separate=args.separate_calls)
+                         evict, separate=args.separate_calls,
+                         oracle_outputs=oracle_out.get("decode16"))
         sec["decode16"] = decode_summary(d, ceilings)
+        sec["decode16"]["parity"] = d["parity"]
         if "decode16" in cpu_sec:
             sec["decode16"]["cpu_baseline"] = cpu_sec["decode16"]
     if not args.no_secondary and wl.name != "decode1":

@@ -47,10 +47,15 @@ def attn_report(gpu_bits: np.ndarray, ora_bits: np.ndarray) -> dict:
 # many ulps of the output).
 MIN_WITHIN_2ULP = 0.999
 
+# (what, report) of every attention comparison in this process, for the
+# session summary
+REPORTS = []
+
 
 def assert_attn_close(gpu_bits, ora_bits, what="", min_within_2ulp=MIN_WITHIN_2ULP):
     r = attn_report(gpu_bits, ora_bits)
     print(f"[attn parity] {what} {r}", flush=True)
+    REPORTS.append((what, r))
     assert r["finite"], what
     assert r["fail"] == 0, (what, r)
     assert r["frac_within_2ulp"] >= min_within_2ulp, (what, r)
