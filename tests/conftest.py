@@ -12,7 +12,8 @@ def pytest_configure(config):
 
 def pytest_terminal_summary(terminalreporter, exitstatus, config):
     """Every attention comparison of the session (max ulp, share within 2
-    bf16 ulp, worst absolute error), so the figures show even under -q."""
+    bf16 ulp, worst absolute and relative error), so the figures show even
+    under -q."""
     try:
         import parity
     except ImportError:
@@ -27,4 +28,4 @@ def pytest_terminal_summary(terminalreporter, exitstatus, config):
     for what, r in parity.REPORTS:
         tr.write_line(f"  {what}: n={r['n']} max_ulp={r['max_ulp']:.1f} "
                       f"within_2ulp={r['frac_within_2ulp']:.5f} max_abs={r['max_abs']:.2e} "
-                      f"fail={r['fail']}")
+                      f"max_rel(|o|>1e-6)={r['max_rel_nonzero']:.2e} fail={r['fail']}")
