@@ -232,3 +232,88 @@ def test_fused_negative_position_writes_nothing():
     assert np.all(LY.to_numpy_bf16(buf.out)[0] == 0)
     want_row = O.fp8_round_rows(LY.to_numpy_bf16(buf.kv_new)[1:2])[0]
     assert np.array_equal(ring[1, 200 % Wn], want_row)
+
+
+def test_fused_long_rows_with_ties():
+    """Score rows of 20000 positions (the sampled-threshold select) through the
+    decode step: three sequences (one sees 301 positions, fewer than k; one a
+    ragged 12345; one all 20000), a 600-way tie group straddling place k in
+    the last two (the key at rank 400 copied over 600 visible positions), the
+    step run eagerly and as two graph replays.  Every run's selection equals
+    the oracle's top-k of the GPU's scores (the same rows each time) and the
+    outputs match the oracle attention."""
+    from indexer_top_sink_amd import v41
+    B, H, D, Wn, HI, DI, k, ratio, L = 3, 16, 128, 128, 64, 128, 512, 4, 20000
+    pos = [4 * 301 - 1, 4 * 12345 - 1, 4 * L - 1]
+    geo = LY.Geometry(n_heads=H, head_dim=D, window=Wn, index_heads=HI, index_dim=DI, topk=k,
+                      ratio=ratio, scale=float(np.float32(1.0 / np.sqrt(D))))
+    seed = 0x5EED7100
+    rng = np.random.default_rng(7)
+    sink = S.normal_f32(seed, S.TAG_SINK, (H,))
+    host = []
+    for b in range(B):
+        s = seed + b
+        kI = S.normal_bf16(s, S.TAG_KI, (L, DI))
+        qI = S.normal_bf16(s, S.TAG_QI, (HI, DI))
+        w = S.uniform_f32(s, S.TAG_W, (HI,), scale=1.0 / 64)
+        n_vis = min(L, (pos[b] + 1) // ratio)
+        if n_vis > k:
+            sc = O.indexer_scores(qI[None], kI, w[None], pos[b], ratio)[0][:n_vis]
+            src = int(np.lexsort((np.arange(n_vis), -sc))[400])
+            kI[rng.choice(n_vis, 600, replace=False)] = kI[src]
+        host.append({"ring": O.fp8_round_rows(S.normal_bf16(s, S.TAG_KV_RING, (Wn, D))),
+                     "latent": S.normal_bf16(s, S.TAG_LATENT, (L, D)), "kI": kI,
+                     "q": S.normal_bf16(s, S.TAG_Q, (H, D)),
+                     "kv_new": S.normal_bf16(s, S.TAG_KV_NEW, (D,)), "qI": qI, "w": w})
+
+    def staged():
+        buf = LY.alloc_decode(geo, B, L, DEV)
+        buf.sink.copy_(torch.from_numpy(sink).to(DEV))
+        for b, h in enumerate(host):
+            buf.ring[b].copy_(LY.to_device_bf16(h["ring"], DEV))
+            buf.latent[b].copy_(LY.to_device_bf16(h["latent"], DEV))
+            buf.kI[b].copy_(LY.to_device_bf16(h["kI"], DEV))
+            buf.q[b].copy_(LY.to_device_bf16(h["q"], DEV))
+            buf.kv_new[b].copy_(LY.to_device_bf16(h["kv_new"], DEV))
+            buf.qI[b].copy_(LY.to_device_bf16(h["qI"], DEV))
+            buf.w[b].copy_(torch.from_numpy(h["w"]).to(DEV))
+        return buf
+
+    pos_dev = torch.tensor(pos, dtype=torch.int32, device=DEV)
+    buf = staged()
+    args = LY.decode_step_args(buf, pos_dev, None)
+    v41.v41_decode_step(args)                       # eager, then two replays
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        v41.v41_decode_step(args)
+    torch.cuda.synchronize()
+    results = []
+    for rep in range(3):
+        if rep:
+            buf.idx.fill_(-7)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+        got = snapshot(buf)
+        say("long rows with ties, run", rep)
+        assert np.array_equal(got["idx"][:, Wn:], O.topk(got["scores"], k, Wn)), rep
+        for b in range(B):
+            n_vis = min(L, (pos[b] + 1) // ratio)
+            assert int((got["idx"][b, Wn:] >= 0).sum()) == min(k, n_vis)
+        results.append(got["idx"])
+    assert all(np.array_equal(results[0], r) for r in results[1:])
+    # the tie groups straddle place k, and their chosen members are the lowest
+    for b in (1, 2):
+        sc = got["scores"][b]
+        vals, counts = np.unique(sc[np.isfinite(sc)], return_counts=True)
+        members = np.nonzero(sc == vals[np.argmax(counts)])[0]
+        chosen = np.intersect1d(members, got["idx"][b, Wn:] - Wn)
+        assert members.size >= 600 and 0 < chosen.size < members.size, b
+        assert chosen.max() < np.setdiff1d(members, chosen).min(), b
+    for b in range(B):
+        ora = O.sparse_attn(got["q"][b:b + 1], got["ring"][b], host[b]["latent"],
+                            got["idx"][b:b + 1], sink, geo.scale)
+        assert_attn_close(got["out"][b:b + 1], ora, f"long-row step attention b={b}")
