@@ -548,7 +548,6 @@ __device__ __forceinline__ f32x4 mfma_pair(u32x2 a, u32x4 b, f32x4 c) {
   return mfma16x16x32(as_bf16x8(aa), as_bf16x8(b), c);
 }
 
-// v combined (max or sum) over the four 16-lane groups of the wavefront.
 // Eight ds_read_b64_tr_b16 at 32-byte steps (eight 16-dim M-tiles of one
 // 16-row K block) and a wait for them.
 __device__ __forceinline__ void tr_load8(u32x2 (&t)[8], uint32_t a) {
