@@ -706,6 +706,31 @@ def run_workload(name, steps, warmup, n_sets, torch, device, evict, rope=False,
             "ms_sep": ms_sep, "sep_stats": sep_stats, "parity": parity}
 
 
+def time_steps_only(name, steps, warmup, n_sets, torch, device, rope=False, separate=False):
+    """The K graph-replayed steps of run_workload alone (the same staging,
+    input sets and step form), nothing else launched in between."""
+    wl = WL.WORKLOADS[name]
+    if wl.mode == "decode":
+        buf0, _ = stage_decode(wl, device)
+        buf0.pos = wl.start_pos
+        buf0.pos_dev = torch.full((wl.batch,), wl.start_pos, dtype=torch.int32, device=device)
+    else:
+        buf0, _ = stage_prefill(wl, device)
+    if rope:
+        attach_rope(buf0, wl, device)
+    sets = [buf0] + [clone_buffers(buf0) for _ in range(n_sets - 1)]
+    for s in sets:
+        s.pos = getattr(buf0, "pos", 0)
+    if wl.mode == "decode" and not separate:
+        fns, form = [[fused_call(s, rope)] for s in sets], "v41_decode_step"
+    else:
+        fns = [[f for _, f in step_calls(s, wl.mode, rope)] for s in sets]
+        form = "separate calls"
+    ms_step, st_stats, _ = timed_steps(fns, steps, warmup, torch)
+    log(f"{name}: {ms_step * 1e3:.1f} us per step ({form}, steps only)")
+    return {"ms_step": ms_step, "step_stats": st_stats, "form": form}
+
+
 # Sources of each kernel: a stored traffic figure holds only while they are
 # unchanged.
 KERNEL_SOURCES = {
@@ -808,6 +833,10 @@ def main():
     ap.add_argument("--output-side", action="store_true",
                     help="time only the output side (inverse rotation, wo_a, wo_b) at decode64 "
                          "and prefill sizes and print that as the JSON line")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time only the graph-replayed steps of the workload (no per-kernel "
+                         "cache-cold timing, ceilings, CPU leg or secondary lines), for a "
+                         "kernel trace of the step as it runs")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MB",
@@ -824,7 +853,7 @@ def main():
     # the oracle first, before anything touches the GPU (its pool forks)
     cpu = None
     oracle_out = {}
-    if not args.no_cpu_baseline and not args.output_side:
+    if not args.no_cpu_baseline and not args.output_side and not args.step_only:
         t0 = time.time()
         cpu = cpu_baseline(wl)
         oracle_out[wl.name] = cpu.pop("_outputs")
@@ -864,6 +893,17 @@ def main():
                           "value": res["decode64"]["us_per_step"], "unit": "us",
                           "higher_is_better": False, "data": "synthetic", "detail": res}),
               flush=True)
+        return
+    if args.step_only:
+        r = time_steps_only(args.workload, args.steps, args.warmup, args.input_sets, torch,
+                            device, rope=args.rope, separate=args.separate_calls)
+        print(json.dumps({"metric": "us per step (graph-replayed steps only)",
+                          "value": round(r["ms_step"] * 1e3, 2), "unit": "us",
+                          "higher_is_better": False, "data": "synthetic",
+                          "config": {"workload": wl.name, "steps": args.steps,
+                                     "input_sets": args.input_sets,
+                                     "step_form": r["form"]},
+                          "step_us": us_stats(r["step_stats"])}), flush=True)
         return
     ceilings = measured_ceilings(torch, device)
     log(f"measured ceilings: {ceilings}")
