@@ -831,7 +831,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=48)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=SECONDARY_WARMUP,
+                    help="untimed warm-up steps before the K timed ones (the default carries "
+                         "the GPU past its clock ramp)")
     ap.add_argument("--workload", default="decode64", choices=sorted(WL.WORKLOADS))
     ap.add_argument("--input-sets", type=int, default=4)
     ap.add_argument("--rope", action="store_true",
