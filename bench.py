@@ -18,7 +18,10 @@ runs on set i mod n, so a set's data was last touched n - 1 steps earlier
 (for the decode workloads more than the 256 MB last-level cache in between).
 One HIP graph holds one step per set and is replayed, with an event after
 each replay: the value is K over the first-to-last event time, and the
-replays give the median and 90th percentile of the per-step time.  Per
+replays give the median and 90th percentile of the per-step time.  Exactly
+W untimed warm-up steps come first (256 by default and for the secondary
+lines: the GPU raises its clocks over tens of milliseconds of sustained
+work).  Per
 kernel: each rep reads a 1 GiB buffer that evicts the last-level cache, then
 launches the kernel once on each input set, directly, between two events, so
 every launch reads its data from HBM; mean, p50 and p90 over the reps of the
@@ -30,7 +33,13 @@ copy and an 8192^3 bf16 torch.mm are reported beside them).
 The CPU baseline is the oracle (plain C), run before the GPU is touched: one
 thread on a bounded sample, and a process pool over the step's sequences
 (tokens) on the host cores available (at most 16), with the core count and
-CPU model; the prefill and decode16 lines carry the same two legs.
+CPU model; the prefill and decode16 lines carry the same two legs.  The
+single-thread leg's oracle results also serve the `parity` entry of each
+line: the GPU step's selected rows and attention output on the same inputs,
+in bf16 ulp of the oracle's.
+
+--step-only times the graph-replayed steps alone (for a kernel trace of the
+step as it runs); --output-side times the output projections.
 
 With --rope the step starts from q and kv rows before their rotation: q is
 rotated in place and the fp8 call becomes the fused rotation + fp8 + ring write
