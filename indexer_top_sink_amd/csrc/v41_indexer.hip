@@ -215,27 +215,47 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(
     keep = lane < n_live ? wkeep[wave][lane] : 0u;
     return lane < n_live ? wlist[wave][lane] : 0;
   };
+  // ---- the query's qI and weights into registers, the first kStages live
+  // blocks in flight, then the query through LDS.  With a candidate mask the
+  // qI loads go first, so that their latency overlaps the mask reads of the
+  // block list (prefill chunk 23.8 -> 20.3 us); without one the key stream
+  // is the critical path and its first blocks go first (issuing qI first
+  // there measured 25.6 -> 26.7 us at decode64)
+  constexpr int kQPer = (16 * HT * KT::CPR + kThreads - 1) / kThreads;
+  u32x4 qv[kQPer];
+  float wv = 0.0f;
+  const uint16_t* qrow = qI + q * n_heads * DI;
+  auto load_query = [&]() {
+#pragma unroll
+    for (int j = 0; j < kQPer; ++j) {
+      const int e = (int)threadIdx.x + j * kThreads;
+      const int h = e / KT::CPR;
+      const int c = e % KT::CPR;
+      qv[j] = (u32x4){0u, 0u, 0u, 0u};
+      if (e < 16 * HT * KT::CPR && h < n_heads)
+        qv[j] = *reinterpret_cast<const u32x4*>(qrow + h * DI + 8 * c);
+    }
+    if (threadIdx.x < 64 && (int)threadIdx.x < n_heads) wv = w[q * n_heads + threadIdx.x];
+  };
+  if (cand != nullptr) load_query();
   int n_live0 = 0;
   uint32_t keep0 = 0u;
   const int32_t list0 = nw > 0 ? chunk_list(0, n_live0, keep0) : 0;
-
-  // ---- first kStages live blocks in flight, then the query through LDS
 #pragma unroll
   for (int s = 0; s < kStages; ++s)
     if (s < n_live0)
       issue_block<DI, kAux>(kb, (part + __builtin_amdgcn_readlane(list0, s) * wpq) * 16,
                             live_end, lane, ring + s * KT::kBytes);
-  {
-    const uint16_t* qrow = qI + q * n_heads * DI;
-    for (int e = threadIdx.x; e < 16 * HT * KT::CPR; e += kThreads) {
-      const int h = e / KT::CPR;
-      const int c = e % KT::CPR;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (h < n_heads) v = *reinterpret_cast<const u32x4*>(qrow + h * DI + 8 * c);
-      *reinterpret_cast<u32x4*>(qs + h * 2 * DI + 16 * (c ^ KT::swz(h))) = v;
-    }
-    if (threadIdx.x < 64) ws[threadIdx.x] = (int)threadIdx.x < n_heads ? w[q * n_heads + threadIdx.x] : 0.0f;
+  if (cand == nullptr) load_query();
+#pragma unroll
+  for (int j = 0; j < kQPer; ++j) {
+    const int e = (int)threadIdx.x + j * kThreads;
+    const int h = e / KT::CPR;
+    const int c = e % KT::CPR;
+    if (e < 16 * HT * KT::CPR)
+      *reinterpret_cast<u32x4*>(qs + h * 2 * DI + 16 * (c ^ KT::swz(h))) = qv[j];
   }
+  if (threadIdx.x < 64) ws[threadIdx.x] = wv;
   lds_barrier();
 
   // lane offsets of its k-step operands in a block (row r16, chunks g + 4kk)
