@@ -1,6 +1,6 @@
 """Comparison helpers for the GPU parity tests (tolerances of the method):
 fp8 rows, window indices and top-k indices bit-exact; indexer scores within
-1e-4 relative (infinities exact); attention outputs within 2 bf16 ulp or 1e-2
+1e-4 relative or the binary32 forward error bound (infinities exact); attention outputs within 2 bf16 ulp or 1e-2
 absolute, with max ulp and max relative error reported."""
 from __future__ import annotations
 
@@ -62,18 +62,44 @@ def assert_attn_close(gpu_bits, ora_bits, what="", min_within_2ulp=MIN_WITHIN_2U
     return r
 
 
-def assert_scores_close(gpu: np.ndarray, ora: np.ndarray, what=""):
+def score_abs_bound(qI: np.ndarray, kI: np.ndarray, w: np.ndarray, t: int, j: int) -> float:
+    """sum_h w[t, h] * sum_d |qI[t, h, d] * kI[j, d]| in double (bf16 bits in)."""
+    q = bf16_f64(qI[t])
+    k = bf16_f64(kI[j])
+    return float((np.asarray(w[t], np.float64) * (np.abs(q) @ np.abs(k))).sum())
+
+
+def assert_scores_close(gpu: np.ndarray, ora: np.ndarray, what="", operands=None):
+    """Scores within SCORE_RTOL of the oracle's.  With operands = (qI [T, HI,
+    DI], kI [L, DI], w [T, HI], tokens) -- row r of gpu / ora is token
+    tokens[r] -- a score that misses the relative leg may still be within the
+    forward error bound of its binary32 arithmetic: products of bf16 values
+    are exact in f32, a DI-term dot product summed in f32 is off by at most
+    (DI - 1) u sum|q k|, the weight multiplies in one rounding and the HI
+    weighted terms sum in HI - 1 more (a dot that rounds across zero moves
+    ReLU by no more than its own error), so |error| <= (DI + HI + 1) u
+    sum_h w_h sum_d |q_hd k_d| to first order, u = 2^-24.  That leg matters
+    where a score is a near-cancellation of few heads; with 64 heads of
+    positive terms the relative leg decides."""
     gpu = np.asarray(gpu, dtype=np.float64)
     ora = np.asarray(ora, dtype=np.float64)
     inf_o = np.isinf(ora)
     assert np.array_equal(np.isinf(gpu), inf_o), (what, "infinity pattern differs")
     assert np.array_equal(gpu[inf_o], ora[inf_o]), what
-    f = ~inf_o
-    err = np.abs(gpu[f] - ora[f])
-    tol = SCORE_RTOL * np.abs(ora[f]) + 1e-30
+    err = np.where(inf_o, 0.0, np.abs(gpu - np.where(inf_o, 0.0, ora)))
+    tol = SCORE_RTOL * np.abs(np.where(inf_o, 0.0, ora)) + 1e-30
     bad = err > tol
-    rel = float((err / np.maximum(np.abs(ora[f]), 1e-30)).max()) if f.any() else 0.0
-    print(f"[score parity] {what} n={int(f.sum())} max_rel={rel:.3e} fail={int(bad.sum())}",
-          flush=True)
+    n_rel = int(bad.sum())
+    if n_rel and operands is not None:
+        qI, kI, w, tokens = operands
+        HI, DI = qI.shape[1], qI.shape[2]
+        for r, j in zip(*np.nonzero(bad)):
+            bound = (DI + HI + 2) * 2.0 ** -24 * score_abs_bound(qI, kI, w, tokens[r], j)
+            if err[r, j] <= tol[r, j] + bound:
+                bad[r, j] = False
+    f = ~inf_o
+    rel = float((err[f] / np.maximum(np.abs(ora[f]), 1e-30)).max()) if f.any() else 0.0
+    print(f"[score parity] {what} n={int(f.sum())} max_rel={rel:.3e} "
+          f"outside_rel={n_rel} fail={int(bad.sum())}", flush=True)
     assert not bad.any(), (what, int(bad.sum()), rel)
     return rel
