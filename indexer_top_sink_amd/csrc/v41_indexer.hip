@@ -114,10 +114,13 @@ __device__ __forceinline__ void issue_block(const uint16_t* kb, int j0, int live
   }
 }
 
-template <int DI, int HT, int NT>
+// F bit 0: keys streamed past the caches (a decode step); bit 1: a
+// candidate mask is given (the two prologue orders below are then separate
+// kernels, so the compiler never joins their loads in flight).
+template <int DI, int HT, int F>
 __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(
     const uint16_t* __restrict__ qI, const uint16_t* __restrict__ kI, int64_t kI_bs,
-    const float* __restrict__ w, const uint8_t* __restrict__ cand, int32_t cand_width,
+    const float* __restrict__ w, const uint8_t* __restrict__ cand_in, int32_t cand_width,
     int32_t cand_block, int32_t n_tokens, int64_t start_pos, const int32_t* __restrict__ pos,
     int32_t ratio, int32_t n_heads, int32_t n_rows, float* __restrict__ scores,
     int64_t scores_ld, int32_t blocks_per_query, FrontParams front, int32_t score_blocks) {
@@ -130,7 +133,8 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(
   constexpr int KS = KT::KS;
   constexpr int kQBytes = 16 * HT * DI * 2;
   constexpr int kRingBytes = kStages * KT::kBytes;
-  constexpr int kAux = NT ? 2 : 0;  // nt: no reuse expected
+  constexpr int kAux = (F & 1) ? 2 : 0;  // no reuse expected
+  const uint8_t* __restrict__ const cand = (F & 2) ? cand_in : nullptr;
   __shared__ __attribute__((aligned(16))) uint8_t smem[kQBytes + 64 * 4 + kWaves * kRingBytes];
   __shared__ int32_t wlist[kWaves][kWave];   // live block lists
   __shared__ uint32_t wkeep[kWaves][kWave];  // and their 16-bit keep masks
@@ -237,16 +241,25 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(
     }
     if (threadIdx.x < 64 && (int)threadIdx.x < n_heads) wv = w[q * n_heads + threadIdx.x];
   };
-  if (cand != nullptr) load_query();
   int n_live0 = 0;
   uint32_t keep0 = 0u;
-  const int32_t list0 = nw > 0 ? chunk_list(0, n_live0, keep0) : 0;
+  int32_t list0 = 0;
+  auto issue_first = [&]() {
 #pragma unroll
-  for (int s = 0; s < kStages; ++s)
-    if (s < n_live0)
-      issue_block<DI, kAux>(kb, (part + __builtin_amdgcn_readlane(list0, s) * wpq) * 16,
-                            live_end, lane, ring + s * KT::kBytes);
-  if (cand == nullptr) load_query();
+    for (int s = 0; s < kStages; ++s)
+      if (s < n_live0)
+        issue_block<DI, kAux>(kb, (part + __builtin_amdgcn_readlane(list0, s) * wpq) * 16,
+                              live_end, lane, ring + s * KT::kBytes);
+  };
+  if constexpr ((F & 2) != 0) {
+    load_query();
+    if (nw > 0) list0 = chunk_list(0, n_live0, keep0);
+    issue_first();
+  } else {
+    if (nw > 0) list0 = chunk_list(0, n_live0, keep0);
+    issue_first();
+    load_query();
+  }
 #pragma unroll
   for (int j = 0; j < kQPer; ++j) {
     const int e = (int)threadIdx.x + j * kThreads;
@@ -347,7 +360,7 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(
   }
 }
 
-template <int DI, int NT>
+template <int DI, int F>
 hipError_t dispatch_heads(int ht, dim3 grid, hipStream_t s, const uint16_t* qI,
                           const uint16_t* kI, int64_t kI_bs, const float* w,
                           const uint8_t* cand, int32_t cand_width, int32_t cand_block,
@@ -356,7 +369,7 @@ hipError_t dispatch_heads(int ht, dim3 grid, hipStream_t s, const uint16_t* qI,
                           int64_t scores_ld, int32_t bpq, const FrontParams& front,
                           int32_t score_blocks) {
 #define V41_IDX_LAUNCH(HT_)                                                                   \
-  hipLaunchKernelGGL((indexer_kernel<DI, HT_, NT>), grid, dim3(kThreads), 0, s, qI, kI,      \
+  hipLaunchKernelGGL((indexer_kernel<DI, HT_, F>), grid, dim3(kThreads), 0, s, qI, kI,       \
                      kI_bs, w, cand, cand_width, cand_block, n_tokens, start_pos, pos,       \
                      ratio, n_heads, n_rows, scores, scores_ld, bpq, front, score_blocks)
   switch (ht) {
@@ -376,13 +389,17 @@ hipError_t dispatch_nt(bool nt, int ht, dim3 grid, hipStream_t s, const uint16_t
                        int64_t start_pos, const int32_t* pos, int32_t ratio, int32_t n_heads,
                        int32_t n_rows, float* scores, int64_t scores_ld, int32_t bpq,
                        const FrontParams& front, int32_t score_blocks) {
-  if (nt)
-    return dispatch_heads<DI, 1>(ht, grid, s, qI, kI, kI_bs, w, cand, cand_width, cand_block,
-                                 n_tokens, start_pos, pos, ratio, n_heads, n_rows, scores,
-                                 scores_ld, bpq, front, score_blocks);
-  return dispatch_heads<DI, 0>(ht, grid, s, qI, kI, kI_bs, w, cand, cand_width, cand_block,
-                               n_tokens, start_pos, pos, ratio, n_heads, n_rows, scores,
-                               scores_ld, bpq, front, score_blocks);
+#define V41_IDX_FLAGS(F_)                                                                     \
+  return dispatch_heads<DI, F_>(ht, grid, s, qI, kI, kI_bs, w, cand, cand_width, cand_block, \
+                                n_tokens, start_pos, pos, ratio, n_heads, n_rows, scores,    \
+                                scores_ld, bpq, front, score_blocks)
+  switch ((nt ? 1 : 0) | (cand != nullptr ? 2 : 0)) {
+    case 1: V41_IDX_FLAGS(1);
+    case 2: V41_IDX_FLAGS(2);
+    case 3: V41_IDX_FLAGS(3);
+    default: V41_IDX_FLAGS(0);
+  }
+#undef V41_IDX_FLAGS
 }
 
 }  // namespace

@@ -146,6 +146,11 @@ def run_indexer(v41, qI, kI, w, start, ratio, cand=None, cand_block=1, B=1, T=No
     (16, 64, 200, 0, 2, 7, 3),          # three sequences of seven tokens
     (64, 128, 40, 0, 1, 2, 1),          # two tokens
     (64, 128, 20, 0, 1, 50, 1),         # the causal bound capped at the row count
+    # a thousand queries and more over short rows (one workgroup per query)
+    (17, 64, 97, 0, 4, 1030, 1),        # odd heads
+    (64, 128, 256, 0, 4, 1024, 1),
+    (4, 32, 1000, 0, 1, 1100, 1),       # 4 heads: near-cancelling scores
+    (16, 64, 200, 0, 2, 600, 2),        # two sequences of 600 tokens
 ])
 def test_indexer_parity(v41, HI, DI, L, start, ratio, T, B):
     say("indexer", HI, DI, L, start, ratio, T, B)
@@ -155,8 +160,10 @@ def test_indexer_parity(v41, HI, DI, L, start, ratio, T, B):
     w = (rng.uniform(0, 1, (B * T, HI)) / 8).astype(np.float32)
     got = run_indexer(v41, qI, kI, w, start, ratio, B=B, T=T)
     for b in range(B):
-        ora = O.indexer_scores(qI[b * T:(b + 1) * T], kI[b], w[b * T:(b + 1) * T], start, ratio)
-        assert_scores_close(got[b * T:(b + 1) * T], ora, f"indexer b={b}")
+        qb, wb = qI[b * T:(b + 1) * T], w[b * T:(b + 1) * T]
+        ora = O.indexer_scores(qb, kI[b], wb, start, ratio)
+        assert_scores_close(got[b * T:(b + 1) * T], ora, f"indexer b={b}",
+                            operands=(qb, kI[b], wb, range(T)))
 
 
 def test_indexer_candidate_mask(v41):
@@ -169,7 +176,7 @@ def test_indexer_candidate_mask(v41):
     cand = (rng.uniform(size=(T, L // blk)) < 0.5).astype(np.uint8)
     got = run_indexer(v41, qI, kI, w, 0, 4, cand=cand, cand_block=blk)
     ora = O.indexer_scores(qI, kI[0], w, 0, 4, cand=cand, cand_block=blk)
-    assert_scores_close(got, ora, "masked")
+    assert_scores_close(got, ora, "masked", operands=(qI, kI[0], w, range(T)))
 
 
 @pytest.mark.parametrize("blk", [1, 5, 8, 16, 24, 64])
@@ -188,7 +195,28 @@ def test_indexer_mask_blocks(v41, blk):
     cand = (rng.uniform(size=(T, nb)) < 0.4).astype(np.uint8)
     got = run_indexer(v41, qI, kI, w, 0, 1, cand=cand, cand_block=blk)
     ora = O.indexer_scores(qI, kI[0], w, 0, 1, cand=cand, cand_block=blk)
-    assert_scores_close(got, ora, f"mask blocks of {blk}")
+    assert_scores_close(got, ora, f"mask blocks of {blk}", operands=(qI, kI[0], w, range(T)))
+
+
+@pytest.mark.parametrize("blk", [5, 16, 64])
+def test_indexer_mask_many_queries(v41, blk):
+    """The masked stream for 1100 tokens over 1000 keys at ratio 1 (every
+    query in a workgroup of its own, up to 63 key blocks each): masked and
+    invisible blocks written -inf, a token's blocks split over its four
+    wavefronts' live lists."""
+    T, HI, DI, L = 1100, 64, 128, 1000
+    say("indexer mask, many queries", blk)
+    rng = np.random.default_rng(300 + blk)
+    qI = bf16_of(rng.standard_normal((T, HI, DI)))
+    kI = bf16_of(rng.standard_normal((1, L, DI)))
+    w = (rng.uniform(0, 1, (T, HI)) / 64).astype(np.float32)
+    nb = (L + blk - 1) // blk
+    cand = (rng.uniform(size=(T, nb)) < 0.4).astype(np.uint8)
+    toks = list(range(0, 40)) + [255, 256, 511, 777, 998, 999, 1000, 1098, 1099]
+    got = run_indexer(v41, qI, kI, w, 0, 1, cand=cand, cand_block=blk)[toks]
+    ora = O.indexer_scores(qI, kI[0], w, 0, 1, cand=cand, cand_block=blk, tokens=toks)
+    assert_scores_close(got, ora, f"masked, many queries, blocks of {blk}",
+                        operands=(qI, kI[0], w, toks))
 
 
 def test_indexer_mask_long_rows(v41):
@@ -204,7 +232,7 @@ def test_indexer_mask_long_rows(v41):
     toks = [0, 1, 17, 1023, 1024, 2999, 4095, 4998, 4999]
     got = run_indexer(v41, qI, kI, w, 0, 1, cand=cand, cand_block=blk)[toks]
     ora = O.indexer_scores(qI, kI[0], w, 0, 1, cand=cand, cand_block=blk, tokens=toks)
-    assert_scores_close(got, ora, "long masked rows")
+    assert_scores_close(got, ora, "long masked rows", operands=(qI, kI[0], w, toks))
 
 
 def test_indexer_zero_keys_give_zero(v41):
