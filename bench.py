@@ -25,7 +25,7 @@ work).  Per
 kernel: each rep reads a 1 GiB buffer that evicts the last-level cache, then
 launches the kernel once on each input set, directly, between two events, so
 every launch reads its data from HBM; mean, p50 and p90 over the reps of the
-per-launch time.  Rooflines use the mean.
+per-launch time (20 untimed launches first, 100 reps).  Rooflines use the mean.
 Fractions are given against the published peaks and against ceilings measured
 in the same run (the library's HBM read and matrix-core probes; a 2 GiB device
 copy and an 8192^3 bf16 torch.mm are reported beside them).
@@ -269,15 +269,20 @@ class CacheEvictor:
         torch.sum(self.buf, dim=0, out=self.sink)
 
 
+KERNEL_WARMUP = 20   # untimed launches of each kernel first
+KERNEL_REPS = 100    # timed reps, each after an eviction
+
+
 def time_kernel(fns, reps, evict, torch):
     """Per-launch ms of one kernel: fns launch it once on each input set.
-    Every rep evicts the last-level cache, then launches fns directly (no
-    graph: the launches queue up behind the eviction, so they run back to
-    back) between two events; returns mean, p50 and p90 over the reps of
-    the per-launch average."""
+    KERNEL_WARMUP untimed launches first (cycling over the sets); then every
+    rep evicts the last-level cache and launches fns directly (no graph: the
+    launches queue up behind the eviction, so they run back to back) between
+    two events; returns mean, p50 and p90 over the reps of the per-launch
+    average."""
     st = torch.cuda.current_stream()
-    for f in fns:
-        f()
+    for i in range(max(KERNEL_WARMUP, len(fns))):
+        fns[i % len(fns)]()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
@@ -700,7 +705,7 @@ def run_workload(name, steps, warmup, n_sets, torch, device, evict, rope=False,
         log(f"{name}{' + rope' if rope else ''}: {ms_step * 1e3:.1f} us per step")
 
     kern = {}
-    reps = max(10, steps // 2)
+    reps = KERNEL_REPS
     for ki, (kname, _) in enumerate(calls[0]):
         fns = [calls[i][ki][1] for i in range(n_sets)]
         kern[kname] = {k: v * 1e3 for k, v in time_kernel(fns, reps, evict, torch).items()}
