@@ -223,8 +223,10 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(
   // blocks in flight, then the query through LDS.  With a candidate mask the
   // qI loads go first, so that their latency overlaps the mask reads of the
   // block list (prefill chunk 23.8 -> 20.3 us); without one the key stream
-  // is the critical path and its first blocks go first (issuing qI first
-  // there measured 25.6 -> 26.7 us at decode64)
+  // is the critical path and its first blocks go first.  The two orders are
+  // separate kernels (F bit 1): joined in one, the compiler made the
+  // keys-first path wait for every load in flight before its query loads
+  // (decode64 24.4 -> 23.7 us once split)
   constexpr int kQPer = (16 * HT * KT::CPR + kThreads - 1) / kThreads;
   u32x4 qv[kQPer];
   float wv = 0.0f;
