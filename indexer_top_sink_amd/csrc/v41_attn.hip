@@ -280,6 +280,9 @@ __global__ __launch_bounds__(kThreads, NS == 2 ? 2 : 1) void attn_kernel(Params 
   const int64_t b = qi / p.n_tokens;
   const int head = blockIdx.y * kHeadsPerBlock + 16 * wave + r16;
   const bool head_ok = head < p.n_heads;
+  // the sink goes out with the first loads (read where it is first needed,
+  // after the prologue's waits, it cost a memory latency of its own)
+  const float sink_in = p.sink[head_ok ? head : 0];  // zeroed below past n_heads
   const int64_t total_rows = p.rows_a_len + p.rows_b_len;
 
   // ---- query fragments (B operand of S^T = G Q^T): head r16, dims 32kk+8g..
@@ -327,7 +330,7 @@ __global__ __launch_bounds__(kThreads, NS == 2 ? 2 : 1) void attn_kernel(Params 
 
   const uint16_t* a_base = p.rows_a + b * p.a_bs;
   const uint16_t* b_base = p.rows_b + b * p.b_bs;
-  const float sink2 = head_ok ? p.sink[head] * kLog2e : 0.0f;
+  const float sink2 = head_ok ? sink_in * kLog2e : 0.0f;
   const float kNegInf = -__builtin_huge_valf();
   float m2 = sink2;  // reference max on the log2 scale
   float l_part = 0.0f;
@@ -926,6 +929,9 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_round_kernel(Params p,
   const int64_t b = qi / p.n_tokens;
   const int head = hg * kNarrowHeads + r16;
   const bool head_ok = head < p.n_heads;
+  // the sink goes out with the first loads (read where it is first needed,
+  // after the prologue's waits, it cost a memory latency of its own)
+  const float sink_in = p.sink[head_ok ? head : 0];  // zeroed below past n_heads
   const int64_t total_rows = p.rows_a_len + p.rows_b_len;
 
   // tiles are 16 consecutive entries of the idx row (an entry outside the
@@ -991,7 +997,7 @@ __global__ __launch_bounds__(kNarrowThreads, 1) void attn_round_kernel(Params p,
     if (e < kNarrowHeads * CPR) *reinterpret_cast<u32x4*>(qs + h * kQStride + 16 * c) = qv[j];
   }
 
-  const float sink2 = head_ok ? p.sink[head] * kLog2e : 0.0f;
+  const float sink2 = head_ok ? sink_in * kLog2e : 0.0f;
   const float kNegInf = -__builtin_huge_valf();
   float m2 = sink2;  // running reference max on the log2 scale (same in every wavefront)
   float l_part = 0.0f;
@@ -1143,17 +1149,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   const int h = e / Q4;
   const int d4 = e - h * Q4;
   const float kNegInf = -__builtin_huge_valf();
-  const float sink2 = sink[h] * kLog2e;
   // splits in chunks of kChunk: a chunk's loads are all issued before any
   // returns, then its maximum updates the running one (a single chunk gives
   // exactly the two-pass form: M over the sink and every split first)
   constexpr int kChunk = 8;
-  float M = sink2;
-  float den = (sink2 == kNegInf) ? 0.0f : 1.0f;  // 2^(sink - M) at M = sink
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < splits; s0 += kChunk) {
-    float2 ml[kChunk];
-    f32x4 v[kChunk];
+  float2 ml[kChunk];
+  f32x4 v[kChunk];
+  auto load_chunk = [&](int s0) {
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
       ml[i] = make_float2(kNegInf, 0.0f);
@@ -1164,6 +1166,16 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
         v[i] = *reinterpret_cast<const f32x4*>(part_o + slot * D + 4 * d4);
       }
     }
+  };
+  // the first chunk's loads go out before the sink's, so that one memory
+  // latency covers them all (read first, the sink was waited for alone)
+  load_chunk(0);
+  const float sink2 = sink[h] * kLog2e;
+  float M = sink2;
+  float den = (sink2 == kNegInf) ? 0.0f : 1.0f;  // 2^(sink - M) at M = sink
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < splits; s0 += kChunk) {
+    if (s0 > 0) load_chunk(s0);
     float Mc = M;
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) Mc = fmaxf(Mc, ml[i].x);
