@@ -25,6 +25,8 @@
 //     positions are written in ascending order, then -1 up to k.
 // The candidate-block selection runs the same select over per-block maxima
 // and writes a byte mask instead of positions.
+#include <float.h>
+
 #include "v41_common.h"
 #include "v41_wave.h"
 
@@ -202,20 +204,19 @@ __device__ __forceinline__ void radix_select(ForKeys for_keys, uint32_t m, uint3
   need = need_r;
 }
 
-// Keys in registers: KPT contiguous positions per thread (n_cols <= NT * KPT).
+// Keys in registers: KPT contiguous positions per thread (n_cols <= NT * KPT,
+// KPT <= 16).
 template <int NT, int KPT>
 __global__ __launch_bounds__(NT) void topk_reg_kernel(const float* __restrict__ scores,
                                                       int32_t n_cols, int64_t scores_ld,
                                                       int32_t k, int32_t offset,
                                                       int32_t* __restrict__ idx,
                                                       int64_t idx_ld) {
+  static_assert(KPT <= 16, "rows of 32 keys per thread take topk_long_kernel");
   // histogram copies: fewer copies make the bin scan cheaper, more spread
   // the atomics of many keys per thread (measured: 2 best at 8 keys per
-  // thread, 4 at 32)
+  // thread)
   __shared__ TopkShared<NT, (KPT <= 8 ? 2 : 4)> sh;
-  constexpr int kCandN = KPT >= 32 ? kCandCap : 1;  // only long rows sample
-  __shared__ uint32_t cand_key[kCandN];
-  __shared__ int32_t cand_pos[kCandN];
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
   const float* __restrict__ srow = scores + row * scores_ld;
@@ -249,110 +250,299 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(const float* __restrict__ 
   }
   uint32_t nv, kmin, kmax;
   // the first radix histogram is cleared before the statistics' barrier,
-  // which then also publishes it; without the sampled threshold the select
-  // (or, when every valid key is taken, one barrier) follows the statistics
-  // before anything rewrites sh.red
+  // which then also publishes it; the select (or, when every valid key is
+  // taken, one barrier) follows the statistics before anything rewrites
+  // sh.red
   for (int i = tid; i < sh.kCopies * kHistStride; i += NT) sh.hist[0][i] = 0u;
-  block_stats<NT, (KPT >= 32)>(nv_t, kmin_t, kmax_t, sh, nv, kmin, kmax);
+  block_stats<NT, false>(nv_t, kmin_t, kmax_t, sh, nv, kmin, kmax);
   const uint32_t m = nv < (uint32_t)k ? nv : (uint32_t)k;
-  if constexpr (KPT < 32) {
-    if (nv <= (uint32_t)k) __syncthreads();
+  uint32_t T = 0u, need = 0u;
+  if (nv <= (uint32_t)k) {
+    __syncthreads();
+  } else {
+    auto all_keys = [&](auto f) {
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) f(key[i]);
+    };
+    radix_select<NT, decltype(all_keys), true>(all_keys, m, kmin, kmax, sh, T, need);
   }
 
-  uint32_t T = 0u, need = 0u;
-  if (nv > (uint32_t)k) {
-    // Sampled threshold (rows of 32 keys per thread): a radix select
-    // over one key per thread picks T0, a key that about r * nv / n_s keys
-    // reach, with r set a few standard deviations above the m * n_s / nv
-    // samples expected among the top m.  With G keys above T0 and E equal:
-    //  - G <= m <= G + E: T0 is the m-th key itself (selection: the G keys
-    //    above it and the first m - G equal ones), no further pass;
-    //  - G > m (and G fits the candidate buffer): the top m lie among the G
-    //    keys above T0, which are compacted in position order and selected
-    //    exactly;
-    //  - otherwise the full select below.
-    bool done = false;
-    if constexpr (KPT >= 32) {
-      uint32_t n_s = 0;
-      (void)block_excl_scan_tot<NT>(key[0] != 0u ? 1u : 0u, sh, n_s);
-      const float expct = (float)m * (float)n_s / (float)nv;
-      const uint32_t r = (uint32_t)ceilf(expct + 3.0f * sqrtf(expct) + 8.0f);
-      if (n_s > 0u && r < n_s) {
-        uint32_t Ts = 0u, need_s = 0u;
-        radix_select<NT>([&](auto f) { f(key[0]); }, r, kmin, kmax, sh, Ts, need_s);
-        const uint32_t T0 = need_s != 0u ? Ts : Ts + 1u;
-        uint32_t cg0 = 0, ce0 = 0;
+  uint32_t cg = 0, ce = 0;
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-          cg0 += key[i] > T0;
-          ce0 += key[i] == T0;
-        }
-        // n_cols <= 32768, so both counts fit 16 bits
-        uint32_t tot = 0;
-        const uint32_t ex0 = block_excl_scan_tot<NT>((cg0 << 16) | ce0, sh, tot);
-        const uint32_t G = tot >> 16, E = tot & 0xFFFFu;
-        if (G <= m && m <= G + E) {
-          T = T0;
-          need = m - G;
-          done = true;
-        } else if (G > m && G <= (uint32_t)kCandCap) {
-          uint32_t at = ex0 >> 16;
+  for (int i = 0; i < KPT; ++i) {
+    cg += key[i] > T;
+    ce += (need != 0u) && (key[i] == T);
+  }
+  // n_cols <= 4096 * 4, so both counts fit 16 bits
+  const uint32_t excl = block_excl_scan<NT, true>((cg << 16) | ce, sh);
+  const uint32_t base_e = excl & 0xFFFFu;
+  uint32_t pos = (excl >> 16) + (base_e < need ? base_e : need);
+  uint32_t er = base_e;
 #pragma unroll
-          for (int i = 0; i < KPT; ++i) {
-            if (key[i] > T0) {
-              cand_key[at] = key[i];
-              cand_pos[at] = lo + i;
-              ++at;
-            }
-          }
-          __syncthreads();
-          uint32_t Tc = 0u, need_c = 0u;
-          radix_select<NT>(
-              [&](auto f) {
-                for (uint32_t i = tid; i < G; i += NT) f(cand_key[i]);
-              },
-              m, T0 + 1u, kmax, sh, Tc, need_c);
-          // output from the candidates: thread t takes CPT consecutive ones
-          constexpr int CPT = kCandCap / NT;
-          const uint32_t c0 = (uint32_t)tid * CPT;
-          uint32_t ck[CPT];
-          uint32_t cg = 0, ce = 0;
+  for (int i = 0; i < KPT; ++i) {
+    if (key[i] > T) {
+      orow[pos++] = lo + i + offset;
+    } else if (need != 0u && key[i] == T) {
+      if (er < need) orow[pos++] = lo + i + offset;
+      ++er;
+    }
+  }
+  for (int32_t i = (int32_t)m + tid; i < k; i += NT) orow[i] = -1;
+}
+
+// Rows of 8193..32768 scores, 32 per thread.  The whole row is taken in one
+// step per wavefront: wavefront w reads its 64 * 32 contiguous scores with
+// consecutive lanes on consecutive 16-byte pieces (whole cache lines per
+// instruction; lanes reading their own 128-byte runs touched 64 lines per
+// instruction), all loads issued before the first is used, parks them in its
+// own LDS region and reads back lane l's 32 contiguous scores (runs padded
+// by 16 bytes, so 16 lanes' reads fall on distinct banks).  The per-score
+// passes then run on the scores as floats: with -inf and NaN excluded and
+// -0 == +0, the float order is the key order, so a comparison costs one
+// instruction where building the key took eight (one workgroup does all of
+// a row's arithmetic, so instructions per score set its time).
+//  1. valid count (wavefront ballots), the row's largest score, and the
+//     sample (key[0] of every thread: one score per 32) count and minimum,
+//     one block reduction;
+//  2. sampled threshold: a radix select over the sample picks T0, a key
+//     that about r * nv / n_s scores reach, r set a few standard deviations
+//     above the m * n_s / nv samples expected among the top m;
+//  3. one pass counts the scores above and at T0 and writes those above it,
+//     (score, position), into the wavefront's region of a candidate buffer;
+//     then with G above T0 and E equal:
+//     - G <= m <= G + E: T0 is the m-th key; the counts give the output
+//       slots directly;
+//     - G > m (and every wavefront's candidates fit its region): an exact
+//       select among the candidates;
+//     - otherwise the full select over the keys.
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) void topk_long_kernel(const float* __restrict__ scores,
+                                                       int32_t n_cols, int64_t scores_ld,
+                                                       int32_t k, int32_t offset,
+                                                       int32_t* __restrict__ idx,
+                                                       int64_t idx_ld) {
+  static_assert(KPT == 32, "one staged row of 32 scores per thread");
+  constexpr int kNW = NT / kWave;
+  constexpr uint32_t kWaveCap = kCandCap / kNW;
+  constexpr int kSeg = KPT + 4;
+  constexpr int kStageBytes = NT * kSeg * 4;
+  static_assert(kStageBytes >= kCandCap * 8, "candidates live in the staging buffer");
+  __shared__ TopkShared<NT, 4> sh;
+  // the load staging, then the candidates (score bits, position)
+  __shared__ __attribute__((aligned(16))) uint8_t raw[kStageBytes];
+  uint2* const cand = reinterpret_cast<uint2*>(raw);
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const float* __restrict__ srow = scores + row * scores_ld;
+  int32_t* __restrict__ orow = idx + row * idx_ld;
+  const int32_t lo = tid * KPT;
+
+  float f[KPT];
+  {
+    constexpr int V = KPT / 4;
+    const int32_t wbase = wave * 64 * KPT;
+    float* const ws = reinterpret_cast<float*>(raw) + wave * 64 * kSeg;
+    float4 g[V];
+    if (((reinterpret_cast<uintptr_t>(srow) & 15u) == 0) && wbase + 64 * KPT <= n_cols) {
 #pragma unroll
-          for (int i = 0; i < CPT; ++i) {
-            ck[i] = (c0 + i < G) ? cand_key[c0 + i] : 0u;
-            cg += ck[i] > Tc;
-            ce += (need_c != 0u) && (ck[i] == Tc);
-          }
-          const uint32_t excl = block_excl_scan<NT, true>((cg << 16) | ce, sh);
-          const uint32_t base_e = excl & 0xFFFFu;
-          uint32_t pos = (excl >> 16) + (base_e < need_c ? base_e : need_c);
-          uint32_t er = base_e;
+      for (int v = 0; v < V; ++v)
+        g[v] = *reinterpret_cast<const float4*>(srow + wbase + v * 256 + lane * 4);
+    } else {
 #pragma unroll
-          for (int i = 0; i < CPT; ++i) {
-            if (ck[i] > Tc) {
-              orow[pos++] = cand_pos[c0 + i] + offset;
-            } else if (need_c != 0u && ck[i] == Tc) {
-              if (er < need_c) orow[pos++] = cand_pos[c0 + i] + offset;
-              ++er;
-            }
-          }
-          for (int32_t i = (int32_t)m + tid; i < k; i += NT) orow[i] = -1;
-          return;
-        }
+      for (int v = 0; v < V; ++v) {
+        const int32_t p = wbase + v * 256 + lane * 4;
+        g[v].x = p + 0 < n_cols ? srow[p + 0] : -INFINITY;
+        g[v].y = p + 1 < n_cols ? srow[p + 1] : -INFINITY;
+        g[v].z = p + 2 < n_cols ? srow[p + 2] : -INFINITY;
+        g[v].w = p + 3 < n_cols ? srow[p + 3] : -INFINITY;
       }
     }
-    if (!done) {
-      auto all_keys = [&](auto f) {
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) f(key[i]);
-      };
-      if constexpr (KPT >= 32)
-        radix_select<NT>(all_keys, m, kmin, kmax, sh, T, need);
-      else
-        radix_select<NT, decltype(all_keys), true>(all_keys, m, kmin, kmax, sh, T, need);
+    for (int v = 0; v < V; ++v) {
+      const int q = v * 256 + lane * 4;
+      *reinterpret_cast<float4*>(ws + (q / KPT) * kSeg + (q % KPT)) = g[v];
+    }
+    // the read-back takes other lanes' writes: a wavefront's LDS operations
+    // are performed in order, so only the compiler must keep them in order
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const float4 h = *reinterpret_cast<const float4*>(ws + lane * kSeg + 4 * v);
+      f[4 * v + 0] = h.x;
+      f[4 * v + 1] = h.y;
+      f[4 * v + 2] = h.z;
+      f[4 * v + 3] = h.w;
     }
   }
 
+  // 1. statistics (f >= -FLT_MAX is false for NaN and -inf, the unselectable
+  // scores; the comparison-select maximum skips them too).  The ballot's
+  // predicate is written as >= -FLT_MAX: the equivalent f > -inf becomes an
+  // ordered not-equal that the ballot lowering turns into the unordered
+  // v_cmp_neq_f32, true for NaN.
+  uint32_t nvw = 0;
+  float mf = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    nvw += (uint32_t)__popcll(__ballot(f[i] >= -FLT_MAX));
+    mf = f[i] > mf ? f[i] : mf;
+  }
+  const uint32_t key0 = score_key(f[0]);
+  // the sample select's histogram is cleared before the statistics'
+  // barrier, which publishes it
+  for (int i = tid; i < sh.kCopies * kHistStride; i += NT) sh.hist[0][i] = 0u;
+  // valid count (<= 32768) in the high half, valid samples (<= NT) in the low
+  uint32_t nvp, kmin_s, kmax;
+  block_stats<NT, true>(((lane == 0 ? nvw : 0u) << 16) | (key0 != 0u ? 1u : 0u),
+                        key0 != 0u ? key0 : 0xFFFFFFFFu, score_key(mf), sh, nvp, kmin_s, kmax);
+  const uint32_t nv = nvp >> 16, n_s = nvp & 0xFFFFu;
+  const uint32_t m = nv < (uint32_t)k ? nv : (uint32_t)k;
+
+  if (nv > (uint32_t)k && n_s > 0u) {
+    const float expct = (float)m * (float)n_s / (float)nv;
+    const uint32_t r = (uint32_t)ceilf(expct + 3.0f * sqrtf(expct) + 8.0f);
+    if (r < n_s) {
+      // 2. T0 from the sample (its own minimum bounds it from below)
+      uint32_t Ts = 0u, need_s = 0u;
+      auto sample = [&](auto g) { g(key0); };
+      radix_select<NT, decltype(sample), true>(sample, r, kmin_s, kmax, sh, Ts, need_s);
+      const uint32_t T0 = need_s != 0u ? Ts : Ts + 1u;
+      // T0 as scores: key > T0 <=> f > t_gt and key == T0 <=> f == t_eq.
+      // Key 0x7FFFFFFF (that of -0, which counts as +0) is no score's key:
+      // above it lies every score >= -0, i.e. above the negative score
+      // closest to zero, and nothing equals it.
+      float t_gt, t_eq;
+      if (T0 == 0x7FFFFFFFu) {
+        t_gt = __uint_as_float(0x80000001u);
+        t_eq = __uint_as_float(0x7FC00000u);
+      } else {
+        t_gt = __uint_as_float((T0 & 0x80000000u) ? (T0 ^ 0x80000000u) : ~T0);
+        t_eq = t_gt;
+      }
+      // 3. counts and candidates in one pass; wavefront totals go to
+      // sh.red[1], which nothing rewrites later, and one barrier publishes
+      // both
+      uint32_t cg0 = 0, ce0 = 0;
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        cg0 += f[i] > t_gt;
+        ce0 += f[i] == t_eq;
+      }
+      // n_cols <= 32768, so both counts fit 16 bits
+      const uint32_t pk = (cg0 << 16) | ce0;
+      const uint32_t incl = wave_incl_scan_u32(pk);
+      const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
+      if ((wtot >> 16) <= kWaveCap) {
+        uint32_t at = (uint32_t)wave * kWaveCap + ((incl - pk) >> 16);
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+          if (f[i] > t_gt) cand[at++] = make_uint2(__float_as_uint(f[i]), (uint32_t)(lo + i));
+        }
+      }
+      if (lane == kWave - 1) sh.red[1][wave] = incl;
+      __syncthreads();
+      uint32_t below = 0, tot = 0, wmax = 0;
+#pragma unroll
+      for (int w = 0; w < kNW; ++w) {
+        const uint32_t c = sh.red[1][w];
+        below += (w < wave) ? c : 0u;
+        tot += c;
+        wmax = max(wmax, c >> 16);
+      }
+      const uint32_t G = tot >> 16, E = tot & 0xFFFFu;
+      if (G <= m && m <= G + E) {
+        // T0 is the m-th key: the G scores above it and the first m - G at it
+        const uint32_t need0 = m - G;
+        const uint32_t excl = below + incl - pk;
+        const uint32_t base_e = excl & 0xFFFFu;
+        uint32_t pos = (excl >> 16) + (base_e < need0 ? base_e : need0);
+        uint32_t er = base_e;
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+          if (f[i] > t_gt) {
+            orow[pos++] = lo + i + offset;
+          } else if (need0 != 0u && f[i] == t_eq) {
+            if (er < need0) orow[pos++] = lo + i + offset;
+            ++er;
+          }
+        }
+        for (int32_t i = (int32_t)m + tid; i < k; i += NT) orow[i] = -1;
+        return;
+      }
+      if (G > m && wmax <= kWaveCap) {
+        // the top m lie among the candidates; wavefront w's sit at
+        // [w * kWaveCap, + its count), in position order
+        constexpr int SPT = kCandCap / NT;
+        uint32_t ckr[SPT];
+#pragma unroll
+        for (int j = 0; j < SPT; ++j) {
+          const int slot = tid + j * NT;
+          const uint32_t cw = sh.red[1][slot / kWaveCap] >> 16;
+          ckr[j] = ((uint32_t)(slot % kWaveCap) < cw) ? score_key(__uint_as_float(cand[slot].x))
+                                                       : 0u;
+        }
+        uint32_t Tc = 0u, need_c = 0u;
+        radix_select<NT>(
+            [&](auto g) {
+#pragma unroll
+              for (int j = 0; j < SPT; ++j) g(ckr[j]);
+            },
+            m, T0 + 1u, kmax, sh, Tc, need_c);
+        // output: thread t takes CPT consecutive slots (one wavefront's
+        // region holds all of them), so slot order is position order
+        constexpr int CPT = kCandCap / NT;
+        const uint32_t c0 = (uint32_t)tid * CPT;
+        const uint32_t cw0 = sh.red[1][c0 / kWaveCap] >> 16;
+        uint32_t ck[CPT];
+        uint32_t cg = 0, ce = 0;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+          ck[i] = ((c0 + i) % kWaveCap < cw0) ? score_key(__uint_as_float(cand[c0 + i].x)) : 0u;
+          cg += ck[i] > Tc;
+          ce += (need_c != 0u) && (ck[i] == Tc);
+        }
+        const uint32_t excl = block_excl_scan<NT, true>((cg << 16) | ce, sh);
+        const uint32_t base_e = excl & 0xFFFFu;
+        uint32_t pos = (excl >> 16) + (base_e < need_c ? base_e : need_c);
+        uint32_t er = base_e;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+          if (ck[i] > Tc) {
+            orow[pos++] = (int32_t)cand[c0 + i].y + offset;
+          } else if (need_c != 0u && ck[i] == Tc) {
+            if (er < need_c) orow[pos++] = (int32_t)cand[c0 + i].y + offset;
+            ++er;
+          }
+        }
+        for (int32_t i = (int32_t)m + tid; i < k; i += NT) orow[i] = -1;
+        return;
+      }
+    }
+  }
+
+  // the full select over the keys (every valid score taken when nv <= k);
+  // the barrier orders the reads of sh.red above before its next writes
+  __syncthreads();
+  uint32_t key[KPT];
+  uint32_t kmin_t = 0xFFFFFFFFu;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    key[i] = score_key(f[i]);
+    if (key[i] != 0u) kmin_t = min(kmin_t, key[i]);
+  }
+  uint32_t T = 0u, need = 0u;
+  if (nv > (uint32_t)k) {
+    uint32_t unused_n, kmin, unused_max;
+    block_stats<NT, true>(0u, kmin_t, 0u, sh, unused_n, kmin, unused_max);
+    radix_select<NT>(
+        [&](auto g) {
+#pragma unroll
+          for (int i = 0; i < KPT; ++i) g(key[i]);
+        },
+        m, kmin, kmax, sh, T, need);
+  }
   uint32_t cg = 0, ce = 0;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
@@ -773,7 +963,8 @@ hipError_t launch_topk_select(const float* scores, int64_t n_sel_rows, int64_t n
   } else if (n_cols <= 1024 * 8) {
     V41_TOPK_REG(1024, 8);
   } else if (n_cols <= 1024 * 32) {
-    V41_TOPK_REG(1024, 32);
+    hipLaunchKernelGGL((topk_long_kernel<1024, 32>), grid, dim3(1024), 0, s, scores, nc,
+                       scores_ld, k, offset, idx, idx_ld);
   } else {
     hipLaunchKernelGGL((topk_mem_kernel<1024>), grid, dim3(1024), 0, s, scores, nc, scores_ld,
                        k, offset, idx, idx_ld);

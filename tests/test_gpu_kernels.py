@@ -271,7 +271,9 @@ def tie_scores(rng, R, L):
                                           (2, 5000, 100, 0), (2, 32768, 512, 128),
                                           (1, 40000, 2048, 7), (64, 8192, 512, 128),
                                           (8, 300, 2048, 3), (6, 512, 64, 128),
-                                          (3, 500, 100, 7), (4, 64, 16, 0)])
+                                          (3, 500, 100, 7), (4, 64, 16, 0),
+                                          (3, 20001, 512, 128), (2, 30722, 700, 5),
+                                          (3, 6001, 512, 0), (2, 3999, 256, 1)])
 def test_topk_parity_ties(v41, R, L, k, offset):
     say("topk", R, L, k, offset)
     rng = np.random.default_rng(R * 7 + L)
@@ -379,6 +381,40 @@ def test_topk_sampled_threshold_paths(v41, L, kpt, layout):
         s[:] = 0.5
         s[:, rng.permutation(L)[:100]] = 3.0
         s[1, ::7] = -0.0
+    got = run_topk(v41, s, k, 128)
+    assert np.array_equal(got, O.topk(s, k, 128))
+
+
+@pytest.mark.parametrize("n_nonneg", [512, 1000])
+def test_topk_long_threshold_at_signed_zero(v41, n_nonneg):
+    """32768-score rows whose sample (every 32nd position) puts the sampled
+    threshold at the boundary between -0 and the negative scores: 36 samples
+    at or above zero (the expected count for k = 512 plus its margin), one of
+    them -0, the other samples tiny negatives down to -2^-125, the row's
+    largest score 1.0, so the first 8-bit digit window starts exactly at -0's
+    key.  With 512 scores at or above zero the threshold is the 512th key
+    (direct output); with 1000, 600 of them +-0, the top 512 come from the
+    candidates and end inside the zero tie group (ties to the lower
+    position, -0 == +0)."""
+    say("topk threshold at -0", n_nonneg)
+    rng = np.random.default_rng(n_nonneg)
+    L, k = 32768, 512
+    s = -rng.uniform(1e-30, 1.0, L).astype(np.float32)
+    samp = np.arange(0, L, 32)
+    s[samp] = -(rng.integers(1, 1 << 20, samp.size) * np.float32(2.0 ** -149)).astype(np.float32)
+    s[samp[0]] = np.float32(-(2.0 ** -125))
+    top = rng.permutation(samp[1:])[:36]
+    s[top[:10]] = 0.0
+    s[top[10:16]] = -0.0
+    s[top[16:]] = rng.uniform(0.1, 0.9, 20).astype(np.float32)
+    others = rng.permutation(np.setdiff1d(np.arange(L), samp))[:n_nonneg - 36]
+    n_zero = 0 if n_nonneg == 512 else 600
+    s[others[:n_zero // 2]] = 0.0
+    s[others[n_zero // 2:n_zero]] = -0.0
+    s[others[n_zero:]] = rng.uniform(0.0, 0.9, others.size - n_zero).astype(np.float32)
+    s[others[-1]] = 1.0
+    assert int((s >= 0).sum()) == n_nonneg
+    s = s[None, :]
     got = run_topk(v41, s, k, 128)
     assert np.array_equal(got, O.topk(s, k, 128))
 
