@@ -421,20 +421,26 @@ __global__ __launch_bounds__(NT) void topk_long_kernel(const float* __restrict__
         t_gt = __uint_as_float((T0 & 0x80000000u) ? (T0 ^ 0x80000000u) : ~T0);
         t_eq = t_gt;
       }
-      // 3. counts and candidates in one pass; wavefront totals go to
-      // sh.red[1], which nothing rewrites later, and one barrier publishes
-      // both
+      // 3. one pass counts the scores above T0 and writes them to the
+      // wavefront's region of the candidate buffer (in position order, when
+      // they fit); wavefront totals go to sh.red[1], which nothing rewrites
+      // later, and one barrier publishes both.  The scores equal to T0 are
+      // counted in the same pass when T0 is a sample key (need_s != 0, ties
+      // at T0 likely: the row may end there), otherwise only if the
+      // candidates cannot settle the row.
+      const bool with_eq = need_s != 0u;
       uint32_t cg0 = 0, ce0 = 0;
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        cg0 += f[i] > t_gt;
-        ce0 += f[i] == t_eq;
+      for (int i = 0; i < KPT; ++i) cg0 += f[i] > t_gt;
+      if (with_eq) {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) ce0 += f[i] == t_eq;
       }
       // n_cols <= 32768, so both counts fit 16 bits
       const uint32_t pk = (cg0 << 16) | ce0;
       const uint32_t incl = wave_incl_scan_u32(pk);
-      const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1);
-      if ((wtot >> 16) <= kWaveCap) {
+      const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1) >> 16;
+      if (wtot <= kWaveCap) {
         uint32_t at = (uint32_t)wave * kWaveCap + ((incl - pk) >> 16);
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
@@ -451,43 +457,53 @@ __global__ __launch_bounds__(NT) void topk_long_kernel(const float* __restrict__
         tot += c;
         wmax = max(wmax, c >> 16);
       }
-      const uint32_t G = tot >> 16, E = tot & 0xFFFFu;
-      if (G <= m && m <= G + E) {
-        // T0 is the m-th key: the G scores above it and the first m - G at it
-        const uint32_t need0 = m - G;
-        const uint32_t excl = below + incl - pk;
-        const uint32_t base_e = excl & 0xFFFFu;
-        uint32_t pos = (excl >> 16) + (base_e < need0 ? base_e : need0);
-        uint32_t er = base_e;
+      const uint32_t G = tot >> 16;
+      if (G <= m) {
+        uint32_t excl = below + incl - pk;
+        if (!with_eq) {
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-          if (f[i] > t_gt) {
-            orow[pos++] = lo + i + offset;
-          } else if (need0 != 0u && f[i] == t_eq) {
-            if (er < need0) orow[pos++] = lo + i + offset;
-            ++er;
-          }
+          for (int i = 0; i < KPT; ++i) ce0 += f[i] == t_eq;
+          excl = block_excl_scan_tot<NT>((cg0 << 16) | ce0, sh, tot);
         }
-        for (int32_t i = (int32_t)m + tid; i < k; i += NT) orow[i] = -1;
-        return;
-      }
-      if (G > m && wmax <= kWaveCap) {
+        const uint32_t E = tot & 0xFFFFu;
+        if (m <= G + E) {
+          // T0 is the m-th key: the G scores above it and the first m - G
+          // at it
+          const uint32_t need0 = m - G;
+          const uint32_t base_e = excl & 0xFFFFu;
+          uint32_t pos = (excl >> 16) + (base_e < need0 ? base_e : need0);
+          uint32_t er = base_e;
+#pragma unroll
+          for (int i = 0; i < KPT; ++i) {
+            if (f[i] > t_gt) {
+              orow[pos++] = lo + i + offset;
+            } else if (need0 != 0u && f[i] == t_eq) {
+              if (er < need0) orow[pos++] = lo + i + offset;
+              ++er;
+            }
+          }
+          for (int32_t i = (int32_t)m + tid; i < k; i += NT) orow[i] = -1;
+          return;
+        }
+      } else if (wmax <= kWaveCap) {
         // the top m lie among the candidates; wavefront w's sit at
-        // [w * kWaveCap, + its count), in position order
-        constexpr int SPT = kCandCap / NT;
+        // [w * kWaveCap, + its count), in position order.  Each wavefront's
+        // lanes take its own region's (lane + 64 s), so slots past the count
+        // cost nothing once a whole wavefront has none.
+        constexpr int SPT = kWaveCap / kWave;
+        const uint32_t cw = sh.red[1][wave] >> 16;
         uint32_t ckr[SPT];
 #pragma unroll
         for (int j = 0; j < SPT; ++j) {
-          const int slot = tid + j * NT;
-          const uint32_t cw = sh.red[1][slot / kWaveCap] >> 16;
-          ckr[j] = ((uint32_t)(slot % kWaveCap) < cw) ? score_key(__uint_as_float(cand[slot].x))
-                                                       : 0u;
+          const uint32_t o = (uint32_t)(lane + j * kWave);
+          ckr[j] = o < cw ? score_key(__uint_as_float(cand[wave * kWaveCap + o].x)) : 0u;
         }
         uint32_t Tc = 0u, need_c = 0u;
         radix_select<NT>(
             [&](auto g) {
 #pragma unroll
-              for (int j = 0; j < SPT; ++j) g(ckr[j]);
+              for (int j = 0; j < SPT; ++j)
+                if ((uint32_t)(lane + j * kWave) < cw) g(ckr[j]);
             },
             m, T0 + 1u, kmax, sh, Tc, need_c);
         // output: thread t takes CPT consecutive slots (one wavefront's
