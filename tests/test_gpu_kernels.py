@@ -419,6 +419,23 @@ def test_topk_long_threshold_at_signed_zero(v41, n_nonneg):
     assert np.array_equal(got, O.topk(s, k, 128))
 
 
+def test_topk_long_candidates_overflow_one_wavefront(v41):
+    """A 32768-score row whose first 2048 positions (one wavefront's share of
+    the row) hold the high scores: the sampled threshold leaves about 990
+    candidates, under the 4096-slot buffer, but some 560 of them in that
+    wavefront's 256-slot region, so the row takes the full select; the
+    second row spreads the same high scores over the whole row (candidate
+    select)."""
+    say("topk candidates overflow one wavefront")
+    rng = np.random.default_rng(77)
+    L, k = 32768, 512
+    s = rng.uniform(0, 1, (2, L)).astype(np.float32)
+    s[0, :2048] = rng.uniform(0.95, 1.0, 2048).astype(np.float32)
+    s[1, rng.permutation(L)[:2048]] = rng.uniform(0.95, 1.0, 2048).astype(np.float32)
+    got = run_topk(v41, s, k, 128)
+    assert np.array_equal(got, O.topk(s, k, 128))
+
+
 # ------------------------------------------------------------------ attention
 def run_attn(v41, q, rows_a, rows_b, idx, sink, scale, B, T, use_ws=True):
     """q [B*T, H, D]; rows_a [B, A, D]; rows_b [B, Lb, D] or None; idx [B*T, width]."""
