@@ -273,7 +273,9 @@ def tie_scores(rng, R, L):
                                           (8, 300, 2048, 3), (6, 512, 64, 128),
                                           (3, 500, 100, 7), (4, 64, 16, 0),
                                           (3, 20001, 512, 128), (2, 30722, 700, 5),
-                                          (3, 6001, 512, 0), (2, 3999, 256, 1)])
+                                          (3, 6001, 512, 0), (2, 3999, 256, 1),
+                                          (2, 32768, 1, 0), (2, 32768, 2048, 3),
+                                          (2, 24576, 2048, 0)])
 def test_topk_parity_ties(v41, R, L, k, offset):
     say("topk", R, L, k, offset)
     rng = np.random.default_rng(R * 7 + L)
@@ -415,6 +417,23 @@ def test_topk_long_threshold_at_signed_zero(v41, n_nonneg):
     s[others[-1]] = 1.0
     assert int((s >= 0).sum()) == n_nonneg
     s = s[None, :]
+    got = run_topk(v41, s, k, 128)
+    assert np.array_equal(got, O.topk(s, k, 128))
+
+
+@pytest.mark.parametrize("n_valid,k", [(600, 512), (300, 512), (5000, 2048), (0, 64)])
+def test_topk_long_mostly_unselectable(v41, n_valid, k):
+    """32768-score rows where all but n_valid scores are NaN or -inf: fewer
+    valid samples than the sampled threshold needs (full select), fewer
+    valid scores than k (every valid one, then -1), none at all."""
+    say("topk long mostly unselectable", n_valid, k)
+    rng = np.random.default_rng(n_valid + k)
+    L = 32768
+    s = np.where(rng.uniform(size=(2, L)) < 0.5, np.float32(np.nan), np.float32(-np.inf))
+    for r in range(2):
+        pos = rng.permutation(L)[:n_valid]
+        s[r, pos] = rng.standard_normal(n_valid).astype(np.float32)
+    s = s.astype(np.float32)
     got = run_topk(v41, s, k, 128)
     assert np.array_equal(got, O.topk(s, k, 128))
 
