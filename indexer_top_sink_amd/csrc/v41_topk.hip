@@ -295,8 +295,9 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(const float* __restrict__ 
 // consecutive lanes on consecutive 16-byte pieces (whole cache lines per
 // instruction; lanes reading their own 128-byte runs touched 64 lines per
 // instruction), all loads issued before the first is used, parks them in its
-// own LDS region and reads back lane l's 32 contiguous scores (runs padded
-// by 16 bytes, so 16 lanes' reads fall on distinct banks).  The per-score
+// own LDS region and reads back lane l's 32 contiguous scores (16-byte
+// chunks swizzled, so 16 lanes' reads fall on distinct banks); the staged
+// row stays there for the candidates' scores.  The per-score
 // passes then run on the scores as floats: with -inf and NaN excluded and
 // -0 == +0, the float order is the key order, so a comparison costs one
 // instruction where building the key took eight (one workgroup does all of
@@ -307,9 +308,9 @@ __global__ __launch_bounds__(NT) void topk_reg_kernel(const float* __restrict__ 
 //  2. sampled threshold: a radix select over the sample picks T0, a key
 //     that about r * nv / n_s scores reach, r set a few standard deviations
 //     above the m * n_s / nv samples expected among the top m;
-//  3. one pass counts the scores above and at T0 and writes those above it,
-//     (score, position), into the wavefront's region of a candidate buffer;
-//     then with G above T0 and E equal:
+//  3. one pass counts the scores above and at T0 and writes the positions of
+//     those above it (from a bit mask per lane) into the wavefront's region
+//     of a candidate buffer; then with G above T0 and E equal:
 //     - G <= m <= G + E: T0 is the m-th key; the counts give the output
 //       slots directly;
 //     - G > m (and every wavefront's candidates fit its region): an exact
@@ -324,13 +325,23 @@ __global__ __launch_bounds__(NT) void topk_long_kernel(const float* __restrict__
   static_assert(KPT == 32, "one staged row of 32 scores per thread");
   constexpr int kNW = NT / kWave;
   constexpr uint32_t kWaveCap = kCandCap / kNW;
-  constexpr int kSeg = KPT + 4;
-  constexpr int kStageBytes = NT * kSeg * 4;
-  static_assert(kStageBytes >= kCandCap * 8, "candidates live in the staging buffer");
+  // the staged row stays in LDS to the end (the candidates are kept as
+  // positions and read their scores from it): wavefront w's 2048 scores at
+  // [w * 2048, + 2048), lane l's 32 as eight 16-byte chunks, chunk c at
+  // l * 8 + (c ^ ((l >> 1) & 7)) so that 16 lanes reading chunk c fall on
+  // distinct banks
+  constexpr int kStageBytes = NT * KPT * 4;
+  static_assert(KPT == 32, "the chunk swizzle assumes 8 chunks per lane");
   __shared__ TopkShared<NT, 4> sh;
-  // the load staging, then the candidates (score bits, position)
-  __shared__ __attribute__((aligned(16))) uint8_t raw[kStageBytes];
-  uint2* const cand = reinterpret_cast<uint2*>(raw);
+  // the staged row, then the candidates' positions
+  __shared__ __attribute__((aligned(16))) uint8_t raw[kStageBytes + kCandCap * 4];
+  const float* const stage = reinterpret_cast<const float*>(raw);
+  uint32_t* const cand = reinterpret_cast<uint32_t*>(raw + kStageBytes);
+  // LDS float index of row position p (p < NT * KPT)
+  auto staged_at = [](uint32_t p) {
+    const uint32_t w = p >> 11, q = p & 2047u, l = q >> 5, c = (q >> 2) & 7u;
+    return (w << 11) + ((l * 8u + (c ^ ((l >> 1) & 7u))) << 2) + (q & 3u);
+  };
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
   const int64_t row = blockIdx.x;
   const float* __restrict__ srow = scores + row * scores_ld;
@@ -341,7 +352,7 @@ __global__ __launch_bounds__(NT) void topk_long_kernel(const float* __restrict__
   {
     constexpr int V = KPT / 4;
     const int32_t wbase = wave * 64 * KPT;
-    float* const ws = reinterpret_cast<float*>(raw) + wave * 64 * kSeg;
+    float* const ws = reinterpret_cast<float*>(raw) + wave * 64 * KPT;
     float4 g[V];
     if (((reinterpret_cast<uintptr_t>(srow) & 15u) == 0) && wbase + 64 * KPT <= n_cols) {
 #pragma unroll
@@ -360,7 +371,8 @@ __global__ __launch_bounds__(NT) void topk_long_kernel(const float* __restrict__
 #pragma unroll
     for (int v = 0; v < V; ++v) {
       const int q = v * 256 + lane * 4;
-      *reinterpret_cast<float4*>(ws + (q / KPT) * kSeg + (q % KPT)) = g[v];
+      const int l = q / KPT, c = (q % KPT) / 4;
+      *reinterpret_cast<float4*>(ws + (l * 8 + (c ^ ((l >> 1) & 7))) * 4) = g[v];
     }
     // the read-back takes other lanes' writes: a wavefront's LDS operations
     // are performed in order, so only the compiler must keep them in order
@@ -369,7 +381,8 @@ __global__ __launch_bounds__(NT) void topk_long_kernel(const float* __restrict__
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
     for (int v = 0; v < V; ++v) {
-      const float4 h = *reinterpret_cast<const float4*>(ws + lane * kSeg + 4 * v);
+      const float4 h =
+          *reinterpret_cast<const float4*>(ws + (lane * 8 + (v ^ ((lane >> 1) & 7))) * 4);
       f[4 * v + 0] = h.x;
       f[4 * v + 1] = h.y;
       f[4 * v + 2] = h.z;
@@ -429,9 +442,10 @@ __global__ __launch_bounds__(NT) void topk_long_kernel(const float* __restrict__
       // at T0 likely: the row may end there), otherwise only if the
       // candidates cannot settle the row.
       const bool with_eq = need_s != 0u;
-      uint32_t cg0 = 0, ce0 = 0;
+      uint32_t gm = 0, ce0 = 0;  // bit i: f[i] above T0
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) cg0 += f[i] > t_gt;
+      for (int i = 0; i < KPT; ++i) gm |= (f[i] > t_gt ? 1u : 0u) << i;
+      const uint32_t cg0 = (uint32_t)__popc(gm);
       if (with_eq) {
 #pragma unroll
         for (int i = 0; i < KPT; ++i) ce0 += f[i] == t_eq;
@@ -442,10 +456,7 @@ __global__ __launch_bounds__(NT) void topk_long_kernel(const float* __restrict__
       const uint32_t wtot = (uint32_t)__builtin_amdgcn_readlane((int)incl, kWave - 1) >> 16;
       if (wtot <= kWaveCap) {
         uint32_t at = (uint32_t)wave * kWaveCap + ((incl - pk) >> 16);
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-          if (f[i] > t_gt) cand[at++] = make_uint2(__float_as_uint(f[i]), (uint32_t)(lo + i));
-        }
+        for (uint32_t mm = gm; mm != 0u; mm &= mm - 1u) cand[at++] = (uint32_t)lo + __builtin_ctz(mm);
       }
       if (lane == kWave - 1) sh.red[1][wave] = incl;
       __syncthreads();
@@ -496,7 +507,7 @@ __global__ __launch_bounds__(NT) void topk_long_kernel(const float* __restrict__
 #pragma unroll
         for (int j = 0; j < SPT; ++j) {
           const uint32_t o = (uint32_t)(lane + j * kWave);
-          ckr[j] = o < cw ? score_key(__uint_as_float(cand[wave * kWaveCap + o].x)) : 0u;
+          ckr[j] = o < cw ? score_key(stage[staged_at(cand[wave * kWaveCap + o])]) : 0u;
         }
         uint32_t Tc = 0u, need_c = 0u;
         radix_select<NT>(
@@ -515,7 +526,7 @@ __global__ __launch_bounds__(NT) void topk_long_kernel(const float* __restrict__
         uint32_t cg = 0, ce = 0;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-          ck[i] = ((c0 + i) % kWaveCap < cw0) ? score_key(__uint_as_float(cand[c0 + i].x)) : 0u;
+          ck[i] = ((c0 + i) % kWaveCap < cw0) ? score_key(stage[staged_at(cand[c0 + i])]) : 0u;
           cg += ck[i] > Tc;
           ce += (need_c != 0u) && (ck[i] == Tc);
         }
@@ -526,9 +537,9 @@ __global__ __launch_bounds__(NT) void topk_long_kernel(const float* __restrict__
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
           if (ck[i] > Tc) {
-            orow[pos++] = (int32_t)cand[c0 + i].y + offset;
+            orow[pos++] = (int32_t)cand[c0 + i] + offset;
           } else if (need_c != 0u && ck[i] == Tc) {
-            if (er < need_c) orow[pos++] = (int32_t)cand[c0 + i].y + offset;
+            if (er < need_c) orow[pos++] = (int32_t)cand[c0 + i] + offset;
             ++er;
           }
         }
